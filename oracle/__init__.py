@@ -1,0 +1,19 @@
+"""fp64 CPU oracle for paged decode and the slot-mapped cache write.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or run anything in this
+package. The HIP library never calls it, and it imports nothing from the HIP
+path (no binding, no kernel, no shared helper); it takes plain numpy arrays.
+
+Every function here is pinned by ``tests/test_oracle.py`` to facts that the
+pages or plain mathematics fix (worked block-table example, permutation and
+sharing invariance, softmax identities, brute force on tiny inputs, a library
+attention routine on contiguous K/V). No function is "parity unpinned".
+"""
+from .paged_attention import (  # noqa: F401
+    attention_weights,
+    gather_tokens,
+    paged_attn_decode,
+    paged_attn_decode_partitioned,
+)
+from .cache_write import kv_cache_write  # noqa: F401

@@ -1,0 +1,33 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def read_golden(name):
+    """Parse a ``key: value`` fixture, skipping ``#`` comment lines."""
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, _, val = line.partition(":")
+            out[key.strip()] = val.strip()
+    return out
+
+
+@pytest.fixture
+def golden():
+    return read_golden

@@ -1,0 +1,151 @@
+"""Invariants of the seeded generator and closed-form byte accounting.
+
+* internal waste below one block per sequence (vLLM notes page, PagedAttention
+  advantages: internal fragmentation at most one block; paper page: only the
+  last block may be partly empty);
+* physical ids distinct except intended sharing; parallel samples share
+  their prompt blocks with reference count 4; the appended token never lands
+  in a shared block;
+* the KV sizing examples printed on the course page.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_260_amd import accounting, workloads
+
+
+@pytest.fixture(scope="module", params=[1, 2, 3, 4, 5])
+def layout(request):
+    return workloads.make(request.param, values=False), request.param
+
+
+def _used_ids(w, lens):
+    ids = []
+    for s, L in enumerate(lens):
+        n = -(-int(L) // w.block_size)
+        ids.append(w.block_tables[s, :n])
+    return ids
+
+
+def test_waste_below_one_block(layout):
+    w, _ = layout
+    after = w.seq_lens_after_write()
+    for s, L in enumerate(after):
+        allocated = int((w.block_tables[s] >= 0).sum())
+        assert allocated * w.block_size - int(L) < w.block_size
+        assert allocated == -(-int(L) // w.block_size)
+
+
+def test_ids_in_range_and_distinct_except_sharing(layout):
+    w, cfg = layout
+    ids = _used_ids(w, w.seq_lens_after_write())
+    flat = np.concatenate(ids)
+    assert flat.min() >= 0 and flat.max() < w.num_blocks
+    counts = np.bincount(flat, minlength=w.num_blocks)
+    assert np.array_equal(counts, w.refcount)
+    if cfg != 5:
+        assert counts.max() == 1
+    else:
+        shared = np.flatnonzero(counts > 1)
+        assert set(np.unique(counts)) <= {0, 1, 4}
+        assert len(shared) == 16 * (1024 // 32)
+        for s in range(w.num_seqs):
+            assert np.all(counts[w.block_tables[s, :32]] == 4)
+
+
+def test_write_slot_is_private_and_next_position(layout):
+    w, _ = layout
+    BS = w.block_size
+    for s in range(w.num_seqs):
+        L = int(w.seq_lens[s])
+        blk, off = divmod(int(w.slot_mapping[s]), BS)
+        assert w.refcount[blk] == 1
+        assert blk == w.block_tables[s, L // BS] and off == L % BS
+    assert len(set(w.slot_mapping.tolist())) == w.num_seqs
+
+
+def test_pool_sizes(layout):
+    w, cfg = layout
+    need = int((w.refcount > 0).sum())
+    if cfg == 1:
+        assert w.num_blocks == 32
+    else:
+        assert w.num_blocks == math.ceil(1.2 * need)
+
+
+def test_config_shapes():
+    expect = {1: (4, 4, 4, 64, 16, torch.float32), 2: (64, 32, 32, 128, 16, torch.bfloat16),
+              3: (128, 32, 8, 128, 16, torch.bfloat16), 4: (4, 32, 8, 128, 16, torch.bfloat16),
+              5: (64, 32, 8, 128, 32, torch.float16)}
+    for cfg, (B, H, Hkv, D, BS, dt) in expect.items():
+        w = workloads.make(cfg, values=False)
+        assert (w.num_seqs, w.n_heads, w.n_kv_heads, w.head_dim, w.block_size, w.dtype) == \
+            (B, H, Hkv, D, BS, dt)
+    w1 = workloads.make(1, values=False)
+    assert w1.scale == 0.125 and w1.seq_lens.min() >= 1 and w1.seq_lens.max() <= 100
+    w3 = workloads.make(3, values=False)
+    assert w3.seq_lens.min() >= 16 and w3.seq_lens.max() <= 4096
+    assert w3.scale == float(np.float32(1 / math.sqrt(128)))
+    w4 = workloads.make(4, values=False)
+    assert w4.seq_lens.tolist() == [32768, 65536, 98304, 131072]
+    w5 = workloads.make(5, values=False)
+    assert np.all((w5.seq_lens >= 1024 + 64) & (w5.seq_lens <= 1024 + 512))
+
+
+def test_seed_reproducible_and_values_rounded():
+    a = workloads.make(1)
+    b = workloads.make(1)
+    for name in ("q", "k_pool", "v_pool", "k_new", "v_new"):
+        assert torch.equal(getattr(a, name), getattr(b, name))
+    assert np.array_equal(a.block_tables, b.block_tables)
+    c = workloads.random_case(3, num_seqs=3, n_heads=4, n_kv_heads=2, head_dim=64, block_size=16,
+                              dtype=torch.bfloat16, max_len=50)
+    assert c.q.dtype == torch.bfloat16
+    # drawing the values does not move the layout draws
+    d = workloads.make(2, values=False)
+    e = workloads.make(2, seed=2602, values=False)
+    assert np.array_equal(d.block_tables, e.block_tables)
+
+
+def test_poison_marks_only_unreadable_slots():
+    w = workloads.make(1, poison=True)
+    BS = w.block_size
+    for s in range(w.num_seqs):
+        L = int(w.seq_lens[s])
+        for j in range(L):
+            assert torch.isfinite(w.k_pool[w.block_tables[s, j // BS], :, j % BS]).all()
+        blk = int(w.block_tables[s, L // BS])
+        assert torch.isnan(w.k_pool[blk, :, L % BS:]).all()
+    assert torch.isnan(w.v_pool[torch.from_numpy(w.refcount == 0)]).all()
+
+
+def test_utilisation_near_full():
+    for cfg, lo in ((2, 0.98), (3, 0.97)):
+        w = workloads.make(cfg, values=False)
+        assert accounting.utilisation(w.seq_lens, w.block_size) > lo
+    w4 = workloads.make(4, values=False)
+    assert accounting.utilisation(w4.seq_lens, 16) == 1.0
+
+
+def test_kv_sizing_examples(golden):
+    g = golden("kv_sizing.txt")
+    ex = dict(kv.split("=") for kv in g["example1"].split())
+    b = accounting.kv_cache_bytes(int(ex["layers"]), int(ex["hidden"]), int(ex["tokens"]),
+                                  int(ex["elem_bytes"]))
+    assert b == int(ex["bytes"]) == 2 ** 30
+    toy = dict(kv.split("=") for kv in g["toy_reserve"].split())
+    mb = accounting.peak_kv_bytes(float(toy["k_mb"]), int(toy["prompt"]) + int(toy["output"]))
+    assert mb == float(toy["mb"])
+
+
+def test_decode_bytes_closed_form():
+    lens = [16, 100, 1]
+    # 117 tokens x 8 heads x 128 dims x (K and V) x 2 bytes, plus Q and O
+    assert accounting.decode_kv_bytes(lens, 8, 128, 2) == 117 * 8 * 128 * 2 * 2
+    assert accounting.decode_qo_bytes(3, 32, 128, 2) == 2 * 3 * 32 * 128 * 2
+    assert accounting.decode_table_bytes(lens, 16) == 4 * (1 + 7 + 1) + 12
+    bt = np.array([[5, 6, -1], [5, 7, -1]])
+    assert accounting.unique_kv_tokens([20, 20], bt, 16) == 16 + 4 + 4
