@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-decode hot path on one MI355X.
+
+One step = the whole hot path over one batch: the slot-mapped cache write of
+one new token per sequence, then paged decode attention over the updated cache
+(``seq_len + 1`` tokens per sequence). Inputs are seeded synthetic tensors of
+the named workload, resident in HBM before timing starts.
+
+Honest bandwidth: MI355X has a 256 MB memory-side cache, so consecutive steps
+rotate over ``R`` device copies of the KV pools whose combined footprint is at
+least 3x that cache; each step reads a pool that was last touched two steps
+earlier (over 700 MB of other traffic in between for the GQA batch).
+
+Prints one JSON line. ``value`` = compulsory HBM bytes of the step (K/V of
+every cached token + Q + O + the written rows) / wall time per step.
+``roofline`` covers the decode call, timed with HIP events on the stream it
+runs on. ``cpu_baseline`` runs the fp64 oracle on the same batch on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from paged_kv_cache_260_amd import _lib, accounting, workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MALL_BYTES = 256 * 2 ** 20     # memory-side (Infinity) cache
+METRIC = "paged decode effective HBM GB/s (% of MI355X peak) + us/batch, GQA bs=128"
+DTYPE_NAMES = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def stream_ceiling(device, nbytes=2 * 2 ** 30, iters=10):
+    """torch's own reduction and copy over a 2 GiB buffer: a measured read ceiling."""
+    x = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=device).normal_()
+    y = torch.empty_like(x)
+    for _ in range(2):
+        x.sum()
+        y.copy_(x)
+    torch.cuda.synchronize()
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e0.record()
+    for _ in range(iters):
+        x.sum()
+    e1.record()
+    for _ in range(iters):
+        y.copy_(x)
+    e2.record()
+    torch.cuda.synchronize()
+    read = nbytes * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    copy = 2 * nbytes * iters / (e1.elapsed_time(e2) * 1e-3) / 1e9
+    del x, y
+    torch.cuda.empty_cache()
+    return read, copy
+
+
+def cpu_baseline(w, lens_after, kp_after, vp_after, budget_s):
+    """The fp64 oracle on the same batch on host cores, repeated for ~budget_s."""
+    import oracle  # test infrastructure: only this leg of the benchmark runs it
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    qn = w.q.float().numpy()
+    kp = kp_after.float().numpy()
+    vp = vp_after.float().numpy()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.paged_attn_decode(qn, kp, vp, w.block_tables, lens_after, w.scale, w.n_heads,
+                                 w.n_kv_heads, w.head_dim, w.block_size)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    per = el / reps
+    nbytes = accounting.decode_compulsory_bytes(lens_after, w.n_heads, w.n_kv_heads, w.head_dim,
+                                                w.elem_bytes)
+    return {"value": round(nbytes / per / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"whole batch ({w.num_seqs} seqs, {int(np.sum(lens_after))} tokens), "
+                      f"{reps} passes in {el:.1f} s, {per * 1e3:.0f} ms/pass; "
+                      f"numpy fp64, one Python thread driving BLAS with {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5],
+                    help="workload (3 = GQA bf16 batch 128, the headline)")
+    ap.add_argument("--replicas", type=int, default=0, help="pool copies to rotate (0 = auto)")
+    ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = automatic)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    _lib.lib()
+    _lib.set_partition_tokens(args.partition)
+
+    log(f"[bench] building workload config {args.config}")
+    w = workloads.make(args.config)
+    lens0 = w.seq_lens
+    lens1 = w.seq_lens_after_write()
+    e = w.elem_bytes
+    pool_bytes = 2 * w.k_pool.numel() * e
+    R = args.replicas or max(3, math.ceil(3 * MALL_BYTES / pool_bytes))
+    log(f"[bench] pools {pool_bytes / 2**20:.0f} MiB x {R} replicas")
+    q = w.q.to(dev)
+    out = torch.empty_like(q)
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    sl = torch.from_numpy(lens1).to(dev)
+    slots = torch.from_numpy(w.slot_mapping).to(dev)
+    kn = w.k_new.to(dev)
+    vn = w.v_new.to(dev)
+    kps = [w.k_pool.to(dev)]
+    vps = [w.v_pool.to(dev)]
+    for _ in range(R - 1):
+        kps.append(kps[0].clone())
+        vps.append(vps[0].clone())
+    stream = torch.cuda.current_stream(dev)
+
+    def step(r, ev=None):
+        _lib.kv_cache_write(kps[r], vps[r], kn, vn, slots, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        _lib.paged_attn_decode(out, q, kps[r], vps[r], bt, sl, w.scale, w.n_heads, w.n_kv_heads,
+                               w.head_dim, w.block_size, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    log(f"[bench] warmup {args.warmup}")
+    for i in range(args.warmup):
+        step(i % R)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(K):
+        step(i % R, evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(stop) / K
+    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    log(f"[bench] wall {wall * 1e3 / K:.4f} ms/step, events {ms_step:.4f} ms/step")
+
+    dec_bytes = accounting.decode_compulsory_bytes(lens1, w.n_heads, w.n_kv_heads, w.head_dim, e)
+    wr_bytes = accounting.write_bytes(int((w.slot_mapping >= 0).sum()), w.n_kv_heads, w.head_dim, e)
+    step_bytes = dec_bytes + wr_bytes
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    dec_mean = float(dec_ms.mean())
+    achieved = dec_bytes / (dec_mean * 1e-3) / 1e9
+    ptok, nparts = _lib.decode_plan(w.n_heads, w.n_kv_heads, w.block_size, w.num_seqs,
+                                    w.max_blocks_per_seq)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_NAMES[w.dtype],
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "batch": w.num_seqs, "n_heads": w.n_heads, "n_kv_heads": w.n_kv_heads,
+            "head_dim": w.head_dim, "block_size": w.block_size,
+            "cached_tokens": int(lens1.sum()), "mean_seq_len": round(float(lens1.mean()), 1),
+            "max_seq_len": int(lens1.max()), "num_blocks": w.num_blocks,
+            "partition_tokens": ptok, "max_partitions": nparts, "pool_replicas": R,
+            "step": "kv_cache_write (1 token/seq) + paged_attn_decode (seq_len+1)",
+        },
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "us_per_batch": round(ms_step * 1e3, 3),
+        "decode_us": {"mean": round(dec_mean * 1e3, 3),
+                      "p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 3),
+                      "p50": round(float(np.percentile(dec_ms, 50)) * 1e3, 3),
+                      "p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 3)},
+        "step_bytes": int(step_bytes),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "kernel": "paged_attn_decode call (decode kernel"
+                               + (" + partition merge kernel)" if nparts > 1 else ")"),
+                     "algorithmic_bytes": int(dec_bytes)},
+        "wall_ms_per_step": round(wall * 1e3 / K, 5),
+    }
+    if not args.no_ceiling:
+        log("[bench] stream ceiling")
+        rd, cp = stream_ceiling(dev)
+        result["stream_ceiling_gbs"] = {"torch_sum_read": round(rd, 1), "torch_copy_rw": round(cp, 1)}
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        torch.cuda.synchronize()
+        kp_after = kps[0].cpu()
+        vp_after = vps[0].cpu()
+        result["cpu_baseline"] = cpu_baseline(w, lens1, kp_after, vp_after, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,259 @@
+// C-ABI layer: argument validation, planning, workspace, kernel dispatch.
+//
+// Every check that can be made from host-side sizes and pointers happens
+// before the first HIP call, so a bad call returns a status without touching
+// the device (and can be exercised on a machine with no GPU).
+#include "pkv.h"
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int status, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return status;
+}
+
+int ok() {
+  g_error.clear();
+  return PKV_OK;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(PKV_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dtype(int32_t d) { return d == PKV_F32 || d == PKV_F16 || d == PKV_BF16; }
+
+int log2_exact(int v) {
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return (1 << s) == v ? s : -1;
+}
+
+std::atomic<int32_t> g_partition_override{0};
+
+// Automatic partition length: sequences up to 512 tokens stay whole; longer
+// ones are cut into 512-token partitions so that one long sequence spreads
+// over many compute units and the merge traffic stays under 2% of the KV bytes.
+constexpr int64_t kAutoPartition = 512;
+
+void plan(int32_t block_size, int32_t max_blocks, int32_t *ptok, int32_t *nparts) {
+  const int64_t max_tokens = (int64_t)max_blocks * block_size;
+  int64_t p = g_partition_override.load();
+  if (p <= 0) p = max_tokens <= kAutoPartition ? ((max_tokens + 15) / 16) * 16 : kAutoPartition;
+  // Longer than a block: whole blocks, so every partition starts on a block
+  // boundary. At most 64 blocks (the kernel keeps their ids in one VGPR).
+  if (p > block_size) p = (p / block_size) * block_size;
+  const int64_t cap = (int64_t)pkv::kMaxPartitionBlocks * block_size;
+  if (p > cap) p = cap;
+  *ptok = (int32_t)p;
+  *nparts = (int32_t)((max_tokens + p - 1) / p);
+}
+
+// Split-partial workspace, one per (device, stream), grown on demand.
+struct Workspace {
+  void *ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int get_workspace(hipStream_t stream, size_t bytes, void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  Workspace &ws = g_ws[{dev, stream}];
+  if (ws.bytes < bytes) {
+    if (ws.ptr) {
+      e = hipStreamSynchronize(stream);
+      if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+      hipFree(ws.ptr);
+      ws.ptr = nullptr;
+      ws.bytes = 0;
+    }
+    const size_t grow = bytes + bytes / 2;
+    e = hipMalloc(&ws.ptr, grow);
+    if (e != hipSuccess) {
+      ws.ptr = nullptr;
+      return hip_fail(e, "hipMalloc (decode workspace)");
+    }
+    ws.bytes = grow;
+  }
+  *out = ws.ptr;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pkv_last_error(void) { return g_error.c_str(); }
+
+int32_t pkv_version(void) { return (1 << 16) | 0; }
+
+int pkv_set_partition_tokens(int32_t tokens) {
+  if (tokens != 0 && (tokens < 16 || tokens > (1 << 20) || tokens % 16 != 0))
+    return fail(PKV_ERR_INVALID, "partition length %d: want 0 or a multiple of 16 in [16, 2^20]",
+                tokens);
+  g_partition_override.store(tokens);
+  return ok();
+}
+
+int pkv_decode_plan(int32_t n_heads, int32_t n_kv_heads, int32_t block_size, int32_t num_seqs,
+                    int32_t max_blocks_per_seq, int32_t *partition_tokens,
+                    int32_t *max_partitions) {
+  (void)n_heads;
+  (void)n_kv_heads;
+  (void)num_seqs;
+  if (block_size < 1 || max_blocks_per_seq < 1)
+    return fail(PKV_ERR_INVALID, "block_size and max_blocks_per_seq must be >= 1");
+  int32_t p, np;
+  plan(block_size, max_blocks_per_seq, &p, &np);
+  if (partition_tokens) *partition_tokens = p;
+  if (max_partitions) *max_partitions = np;
+  return ok();
+}
+
+int pkv_paged_attn_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
+                          const int32_t *block_tables, const int32_t *seq_lens, float scale,
+                          int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t num_seqs, int32_t max_blocks_per_seq,
+                          int64_t num_blocks, int32_t dtype, void *stream) {
+  if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID, "unknown dtype %d", dtype);
+  if (num_seqs < 0 || num_seqs > 65535)
+    return fail(PKV_ERR_INVALID, "num_seqs %d outside [0, 65535]", num_seqs);
+  if (n_heads < 1 || n_kv_heads < 1)
+    return fail(PKV_ERR_INVALID, "n_heads %d and n_kv_heads %d must be >= 1", n_heads, n_kv_heads);
+  if (n_heads % n_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "n_heads %d is not a multiple of n_kv_heads %d", n_heads,
+                n_kv_heads);
+  const int group = n_heads / n_kv_heads;
+  if (group > 256) return fail(PKV_ERR_UNSUPPORTED, "n_heads / n_kv_heads = %d > 256", group);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d: built for 64 and 128", head_dim);
+  const int bshift = log2_exact(block_size);
+  if (block_size < 16 || block_size > 128 || bshift < 0)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d: built for 16, 32, 64, 128", block_size);
+  if (max_blocks_per_seq < 1)
+    return fail(PKV_ERR_INVALID, "max_blocks_per_seq %d must be >= 1", max_blocks_per_seq);
+  if (num_blocks < 1) return fail(PKV_ERR_INVALID, "num_blocks %lld must be >= 1", (long long)num_blocks);
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID, "scale is not finite");
+  if ((int64_t)max_blocks_per_seq * block_size > (int64_t)INT32_MAX)
+    return fail(PKV_ERR_INVALID, "max_blocks_per_seq * block_size exceeds int32");
+  if (num_seqs == 0) return ok();
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens)
+    return fail(PKV_ERR_INVALID, "null array pointer");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(PKV_ERR_INVALID, "q, out, k_pool and v_pool must be 16-byte aligned");
+
+  pkv::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.num_seqs = num_seqs;
+  a.n_heads = n_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.group = group;
+  const int gt = pkv::decode_head_tile(group);
+  a.head_chunks = (group + gt - 1) / gt;
+  a.block_size = block_size;
+  a.block_shift = bshift;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  plan(block_size, max_blocks_per_seq, &a.partition_tokens, &a.max_parts);
+  if (a.max_parts > 65535)
+    return fail(PKV_ERR_INVALID, "%d partitions exceed the grid limit; raise the partition length",
+                a.max_parts);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (a.max_parts > 1) {
+    const size_t rows = (size_t)num_seqs * n_heads * a.max_parts;
+    const size_t acc_bytes = rows * head_dim * sizeof(float);
+    void *ws = nullptr;
+    int rc = get_workspace(st, acc_bytes + rows * sizeof(float2), &ws);
+    if (rc != PKV_OK) return rc;
+    a.part_acc = static_cast<float *>(ws);
+    a.part_ml = reinterpret_cast<float2 *>(static_cast<char *>(ws) + acc_bytes);
+  }
+  hipError_t e = pkv::launch_decode(static_cast<pkv::DType>(dtype), head_dim, a, st);
+  if (e != hipSuccess) return hip_fail(e, "paged decode launch");
+  return ok();
+}
+
+int pkv_kv_cache_write(void *k_pool, void *v_pool, const void *k_new, const void *v_new,
+                       const int32_t *slot_mapping, int32_t num_tokens, int32_t n_kv_heads,
+                       int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t dtype,
+                       void *stream) {
+  if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID, "unknown dtype %d", dtype);
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID, "num_tokens %d < 0", num_tokens);
+  if (n_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1)
+    return fail(PKV_ERR_INVALID, "n_kv_heads, head_dim, block_size, num_blocks must be >= 1");
+  const int64_t row_bytes = (int64_t)head_dim * pkv::dtype_bytes(static_cast<pkv::DType>(dtype));
+  if (row_bytes % 16 != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim * element size = %lld bytes, not a multiple of 16",
+                (long long)row_bytes);
+  if ((int64_t)n_kv_heads * (row_bytes / 16) * 2 > (int64_t)INT32_MAX)
+    return fail(PKV_ERR_INVALID, "row too large");
+  if (num_tokens == 0) return ok();
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping)
+    return fail(PKV_ERR_INVALID, "null array pointer");
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(PKV_ERR_INVALID, "pools and new rows must be 16-byte aligned");
+  pkv::CacheWriteArgs a{};
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.n_kv_heads = n_kv_heads;
+  a.row_chunks = (int32_t)(row_bytes / 16);
+  a.block_size = block_size;
+  a.num_slots = num_blocks * block_size;
+  hipError_t e = pkv::launch_cache_write(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "cache write launch");
+  return ok();
+}
+
+int pkv_release_workspace(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  int rc = PKV_OK;
+  for (auto &kv : g_ws) {
+    if (!kv.second.ptr) continue;
+    int prev = 0;
+    hipGetDevice(&prev);
+    hipSetDevice(kv.first.first);
+    hipError_t e = hipStreamSynchronize(kv.first.second);
+    if (e == hipSuccess) e = hipFree(kv.second.ptr);
+    hipSetDevice(prev);
+    if (e != hipSuccess) rc = hip_fail(e, "releasing workspace");
+    kv.second = Workspace{};
+  }
+  g_ws.clear();
+  return rc == PKV_OK ? ok() : rc;
+}
+
+}  // extern "C"

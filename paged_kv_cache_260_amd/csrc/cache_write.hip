@@ -1,0 +1,50 @@
+// Slot-mapped KV cache write for CDNA4 (gfx950).
+//
+// Each new token's K and V rows (all KV heads) are copied into the pool slot
+// the scheduler allocated for it: block slot / block_size, offset
+// slot % block_size (vLLM notes page, "V1 engine": slots are allocated before
+// the forward pass; vLLM paper page: a sequence grows one block at a time).
+// The copy is bitwise, in 16-byte units; a negative slot (padding) or a slot
+// past the pool is skipped, so the kernel never writes out of bounds.
+#include "kernels.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kWriteThreads = 256;
+
+__global__ __launch_bounds__(kWriteThreads) void kv_cache_write_kernel(CacheWriteArgs a) {
+  const int units = a.n_kv_heads * a.row_chunks;  // 16-byte units per token, per pool
+  const uint4 *kn = static_cast<const uint4 *>(a.k_new);
+  const uint4 *vn = static_cast<const uint4 *>(a.v_new);
+  uint4 *kp = static_cast<uint4 *>(a.k_pool);
+  uint4 *vp = static_cast<uint4 *>(a.v_pool);
+  for (int t = blockIdx.x; t < a.num_tokens; t += gridDim.x) {
+    const int64_t slot = a.slot_mapping[t];
+    if (slot < 0 || slot >= a.num_slots) continue;
+    const int64_t blk = slot / a.block_size;
+    const int64_t off = slot - blk * a.block_size;
+    for (int u = threadIdx.x; u < 2 * units; u += kWriteThreads) {
+      const bool is_v = u >= units;
+      const int uu = is_v ? u - units : u;
+      const int head = uu / a.row_chunks;
+      const int c = uu - head * a.row_chunks;
+      const int64_t src = (int64_t)t * units + uu;
+      const int64_t dst = ((blk * a.n_kv_heads + head) * a.block_size + off) * a.row_chunks + c;
+      if (is_v)
+        vp[dst] = vn[src];
+      else
+        kp[dst] = kn[src];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t stream) {
+  const int grid = a.num_tokens < 65536 ? a.num_tokens : 65536;
+  hipLaunchKernelGGL(kv_cache_write_kernel, dim3(grid), dim3(kWriteThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

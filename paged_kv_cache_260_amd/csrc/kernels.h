@@ -1,0 +1,64 @@
+// Internal launch interface between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+inline int dtype_bytes(DType t) { return t == DType::F32 ? 4 : 2; }
+
+// Tokens per decode tile: one MFMA column block (16 tokens of one KV head).
+constexpr int kTileTokens = 16;
+// Waves per decode workgroup.
+constexpr int kDecodeWaves = 4;
+// A decode partition spans at most this many blocks: their ids sit one per
+// lane in a single VGPR.
+constexpr int kMaxPartitionBlocks = 64;
+
+struct DecodeArgs {
+  void *out;
+  const void *q;
+  const void *k_pool;
+  const void *v_pool;
+  const int32_t *block_tables;
+  const int32_t *seq_lens;
+  float scale_log2;        // softmax scale * log2(e): scores live in base-2 units
+  int32_t num_seqs;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t group;           // n_heads / n_kv_heads
+  int32_t head_chunks;     // ceil(group / head tile)
+  int32_t block_size;
+  int32_t block_shift;     // log2(block_size)
+  int32_t max_blocks;      // block_tables row width
+  int64_t num_blocks;
+  int32_t partition_tokens;
+  int32_t max_parts;
+  float *part_acc;         // [num_seqs * n_heads * max_parts, head_dim] (only when max_parts > 1)
+  float2 *part_ml;         // [num_seqs * n_heads * max_parts] (max in base-2 units, sum)
+};
+
+// Head tile: query heads of one KV head processed by one workgroup (1, 2, 4, 8 or 16).
+int decode_head_tile(int group);
+
+hipError_t launch_decode(DType dt, int head_dim, const DecodeArgs &a, hipStream_t stream);
+
+struct CacheWriteArgs {
+  void *k_pool;
+  void *v_pool;
+  const void *k_new;
+  const void *v_new;
+  const int32_t *slot_mapping;
+  int32_t num_tokens;
+  int32_t n_kv_heads;
+  int32_t row_chunks;      // head_dim * elem_bytes / 16
+  int32_t block_size;
+  int64_t num_slots;       // num_blocks * block_size
+};
+
+hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,119 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments with a status before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from paged_kv_cache_260_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libpkv.so not built (python -m paged_kv_cache_260_amd.build)")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*PKV_API\s+(?:int|int32_t|const char \*)\s*(pkv_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("pkv_paged_attn_decode", "pkv_kv_cache_write", "pkv_last_error"):
+        assert required in names
+    assert set(names) == set(_lib._SIGNATURES), "binding and header disagree"
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (pkv_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def _decode(**over):
+    args = dict(out=16, q=16, k_pool=16, v_pool=16, block_tables=16, seq_lens=16, scale=0.125,
+                n_heads=32, n_kv_heads=8, head_dim=128, block_size=16, num_seqs=4,
+                max_blocks_per_seq=8, num_blocks=64, dtype=2, stream=None)
+    args.update(over)
+    return _lib.lib().pkv_paged_attn_decode(*args.values())
+
+
+def _write(**over):
+    args = dict(k_pool=16, v_pool=16, k_new=16, v_new=16, slot_mapping=16, num_tokens=4,
+                n_kv_heads=8, head_dim=128, block_size=16, num_blocks=64, dtype=2, stream=None)
+    args.update(over)
+    return _lib.lib().pkv_kv_cache_write(*args.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(n_heads=30), _lib.PKV_ERR_INVALID),            # not a multiple of n_kv_heads
+    (dict(n_kv_heads=0), _lib.PKV_ERR_INVALID),
+    (dict(head_dim=96), _lib.PKV_ERR_UNSUPPORTED),
+    (dict(block_size=8), _lib.PKV_ERR_UNSUPPORTED),
+    (dict(block_size=48), _lib.PKV_ERR_UNSUPPORTED),
+    (dict(dtype=7), _lib.PKV_ERR_INVALID),
+    (dict(q=None), _lib.PKV_ERR_INVALID),
+    (dict(k_pool=24), _lib.PKV_ERR_INVALID),              # misaligned
+    (dict(num_seqs=-1), _lib.PKV_ERR_INVALID),
+    (dict(num_seqs=70000), _lib.PKV_ERR_INVALID),
+    (dict(max_blocks_per_seq=0), _lib.PKV_ERR_INVALID),
+    (dict(num_blocks=0), _lib.PKV_ERR_INVALID),
+    (dict(scale=float("inf")), _lib.PKV_ERR_INVALID),
+    (dict(n_heads=8 * 512), _lib.PKV_ERR_UNSUPPORTED),   # group of 512
+])
+def test_decode_rejects_bad_arguments(over, status):
+    assert _decode(**over) == status
+    assert _lib.last_error() != ""
+
+
+def test_decode_empty_batch_is_noop():
+    assert _decode(num_seqs=0, q=None, out=None) == _lib.PKV_OK
+    assert _lib.last_error() == ""
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(num_tokens=-1), _lib.PKV_ERR_INVALID),
+    (dict(head_dim=4, dtype=2), _lib.PKV_ERR_UNSUPPORTED),   # 8-byte rows
+    (dict(slot_mapping=None), _lib.PKV_ERR_INVALID),
+    (dict(v_new=8), _lib.PKV_ERR_INVALID),
+    (dict(dtype=-1), _lib.PKV_ERR_INVALID),
+    (dict(block_size=0), _lib.PKV_ERR_INVALID),
+])
+def test_write_rejects_bad_arguments(over, status):
+    assert _write(**over) == status
+
+
+def test_write_empty_is_noop():
+    assert _write(num_tokens=0, k_new=None) == _lib.PKV_OK
+
+
+def test_partition_plan():
+    assert _lib.decode_plan(32, 8, 16, 128, 257) == (512, 9)      # 4112 tokens -> 9 x 512
+    assert _lib.decode_plan(4, 4, 16, 4, 7) == (112, 1)           # short tables stay whole
+    assert _lib.decode_plan(32, 8, 16, 4, 8193) == (512, 257)
+    _lib.set_partition_tokens(64)
+    try:
+        assert _lib.decode_plan(32, 8, 16, 4, 10) == (64, 3)
+        _lib.set_partition_tokens(4096)                           # capped at 64 blocks
+        assert _lib.decode_plan(32, 8, 16, 4, 1000) == (1024, 16)
+        _lib.set_partition_tokens(8176)                           # whole blocks, then the cap
+        assert _lib.decode_plan(32, 8, 128, 4, 200) == (8064, 4)
+        _lib.set_partition_tokens(48)                             # shorter than a block: kept
+        assert _lib.decode_plan(32, 8, 64, 4, 3) == (48, 4)
+    finally:
+        _lib.set_partition_tokens(0)
+    for bad in (17, -16, 8, 1 << 21):
+        with pytest.raises(_lib.PkvError):
+            _lib.set_partition_tokens(bad)
+
+
+def test_version():
+    assert _lib.version() >> 16 == 1
