@@ -51,10 +51,12 @@ int log2_exact(int v) {
 
 std::atomic<int32_t> g_partition_override{0};
 
-// Automatic partition length: sequences up to 512 tokens stay whole; longer
-// ones are cut into 512-token partitions so that one long sequence spreads
-// over many compute units and the merge traffic stays under 2% of the KV bytes.
-constexpr int64_t kAutoPartition = 512;
+// Automatic partition length: sequences up to 1024 tokens stay whole; longer
+// ones are cut into 1024-token partitions, so one long sequence spreads over
+// many CUs while merge traffic stays under 1% of the KV bytes. (Measured on
+// MI355X: 1024 is as fast as or faster than 512 on every batch shape tried;
+// shorter partitions lose to per-workgroup startup cost.)
+constexpr int64_t kAutoPartition = 1024;
 
 void plan(int32_t block_size, int32_t max_blocks, int32_t *ptok, int32_t *nparts) {
   const int64_t max_tokens = (int64_t)max_blocks * block_size;
@@ -69,7 +71,8 @@ void plan(int32_t block_size, int32_t max_blocks, int32_t *ptok, int32_t *nparts
   *nparts = (int32_t)((max_tokens + p - 1) / p);
 }
 
-// Split-partial workspace, one per (device, stream), grown on demand.
+// Split-partial workspace, one per (device, stream), grown on demand:
+//   [part_acc: rows x D floats][part_ml: rows x float2], rows = num_seqs * n_heads * max_parts.
 struct Workspace {
   void *ptr = nullptr;
   size_t bytes = 0;
@@ -185,9 +188,9 @@ int pkv_paged_attn_decode(void *out, const void *q, const void *k_pool, const vo
   a.max_blocks = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   plan(block_size, max_blocks_per_seq, &a.partition_tokens, &a.max_parts);
-  if (a.max_parts > 65535)
-    return fail(PKV_ERR_INVALID, "%d partitions exceed the grid limit; raise the partition length",
-                a.max_parts);
+  if ((int64_t)num_seqs * a.max_parts * n_kv_heads * a.head_chunks > (int64_t)INT32_MAX)
+    return fail(PKV_ERR_INVALID, "%d sequences x %d partitions x %d heads: too many workgroups",
+                num_seqs, a.max_parts, n_kv_heads);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (a.max_parts > 1) {
     const size_t rows = (size_t)num_seqs * n_heads * a.max_parts;

@@ -130,23 +130,60 @@ __device__ __forceinline__ float readlane_f(float x, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
 
+template <typename T> struct Pv;  // 4-element operand of the 16x16x16 MFMA
+template <> struct Pv<__bf16> {
+  typedef __bf16 v4 __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ f32x4_t mfma(v4 a, v4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Pv<_Float16> {
+  typedef _Float16 v4 __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ f32x4_t mfma(v4 a, v4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  }
+};
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// ds_read_b64_tr_b16: within each 16-lane group, output lane j receives
+// element (j % 4) of the 8-byte chunks addressed by lanes j / 4 + 4 r,
+// r = 0..3 -- one column of a 4-row block per lane.
+template <typename T>
+__device__ __forceinline__ typename Pv<T>::v4 lds_read_tr(const void *p) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4_t *)(__attribute__((address_space(3))) void *)(p));
+  return __builtin_bit_cast(typename Pv<T>::v4, v);
+}
+
 template <typename T, int D, int GT> struct Cfg {
   static constexpr int kEpc = Elem<T>::kPerChunk;        // elements per 16-byte chunk
   static constexpr int kCh = D / kEpc;                   // chunks per token row
   static constexpr int kLoads = kTileTokens * kCh / 64;  // 16-byte loads per lane per tile
-  static constexpr int kSteps = kCh / 4;                 // MFMA steps per tile
-  static constexpr int kRows = 64 / kCh;                 // token rows in the V layout
+  static constexpr int kSteps = kCh / 4;                 // QK MFMA steps per tile
+  static constexpr int kRows = 64 / kCh;                 // token rows in the VALU V layout
   static constexpr int kNW = kDecodeWaves;
-  // LDS carve-up (bytes)
-  static constexpr int kKstBytes = kTileTokens * kCh * 16;            // per wave
-  static constexpr int kPstBytes = kTileTokens * GT * 4;              // per wave
-  static constexpr int kKstOff = 0;
-  static constexpr int kPstOff = kKstOff + kNW * kKstBytes;
-  static constexpr int kAccOff = kPstOff + kNW * kPstBytes;
-  static constexpr int kMlOff = kAccOff + kNW * GT * D * 4;
+  // P*V on MFMA for 16-bit storage (V read transposed from LDS); fp32 storage
+  // keeps P*V on the VALU.
+  static constexpr bool kPvMfma = sizeof(T) == 2;
+  static constexpr int kDimBlocks = D / 16;              // 16-dim output blocks (MFMA path)
+  // LDS carve-up (bytes). Each wave owns one region: during the tile loop it
+  // holds the staged K tile, V tile (MFMA path) and P; afterwards the wave's
+  // partial accumulator (GT x D fp32) for the workgroup merge.
+  static constexpr int kKstBytes = kTileTokens * kCh * 16;
+  static constexpr int kVstBytes = kPvMfma ? kTileTokens * kCh * 16 : 0;
+  static constexpr int kPstBytes = kPvMfma ? 2 * 16 * 16 * 2 : kTileTokens * GT * 4;
+  static constexpr int kStageBytes = kKstBytes + kVstBytes + kPstBytes;
+  static constexpr int kWaveBytes = kStageBytes > GT * D * 4 ? kStageBytes : GT * D * 4;
+  static constexpr int kKstOff = 0;                      // within a wave region
+  static constexpr int kVstOff = kKstBytes;
+  static constexpr int kPstOff = kKstBytes + kVstBytes;
+  static constexpr int kMlOff = kNW * kWaveBytes;        // workgroup-wide
   static constexpr int kBadOff = kMlOff + kNW * GT * 8;
   static constexpr int kSmem = kBadOff + kNW * 4;
   static_assert(kCh % 4 == 0 && 64 % kCh == 0, "head_dim must give 8, 16 or 32 chunks");
+  static_assert(!kPvMfma || kCh == 8 || kCh == 16, "MFMA P*V path: 8 or 16 chunks per row");
   static_assert(GT >= 1 && GT <= 16, "head tile");
 };
 
@@ -155,6 +192,13 @@ template <typename T, int D, int GT> struct Cfg {
 template <int kCh> __device__ __forceinline__ int kst_slot(int tr, int ch) {
   const int sw = (kCh >= 16 ? tr : (tr >> 1)) & (kCh - 1);
   return tr * kCh + (ch ^ sw);
+}
+// XOR pattern of a staged V tile. Transposed reads of one 16-dim block touch
+// two adjacent chunks (2b, 2b+1) of 4 consecutive tokens per 16-lane group;
+// an even pattern that differs across those tokens puts the 8 chunks in 8
+// distinct bank groups (and keeps chunk pairs together: (2b + h) ^ sw = (2b ^ sw) + h).
+template <int kCh> __device__ __forceinline__ int vst_swz(int tr) {
+  return kCh >= 16 ? (2 * tr) & 15 : 2 * ((tr >> 1) & 3);
 }
 
 template <typename T, int D, int GT>
@@ -168,15 +212,44 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(DecodeA
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = blockIdx.x / a.head_chunks;
-  const int hc = blockIdx.x - g * a.head_chunks;
-  const int s = blockIdx.y;
-  const int part = blockIdx.z;
+  // Work item of this workgroup. The hardware deals workgroup i to XCD i % 8
+  // and, within it, to shader engine (i / 8) % 4, each engine filling its own
+  // CUs. Order: unit (KV head x query-head chunk) fastest, so the sequences a
+  // KV head serves stay on one XCD and its L2 (shared-prefix blocks are read
+  // together); then sequence, then partition, so the empty tail partitions of
+  // short sequences come last; and the sequence index rotated by the
+  // partition index, so one long sequence's partitions cycle through all
+  // engines instead of piling onto one.
+  const int units = a.n_kv_heads * a.head_chunks;
+  const int64_t lin = blockIdx.x;
+  const int unit = (int)(lin % units);
+  const int64_t r = lin / units;
+  const int part = (int)(r / a.num_seqs);
+  const int s = (int)((r % a.num_seqs + a.num_seqs - part % a.num_seqs) % a.num_seqs);
+  const int g = unit / a.head_chunks;
+  const int hc = unit - g * a.head_chunks;
   const int H = a.n_heads;
   const int head0 = g * a.group + hc * GT;
   const int nh = min(GT, a.group - hc * GT);
   T *out = static_cast<T *>(a.out);
 
+  const int P = a.partition_tokens;
+  const int start = part * P;
+  const int kg = lane >> 4;
+  const int n = lane & 15;
+  // Issue the length, the partition's table entries and q together; none of
+  // these addresses depends on the length. Table entries past the sequence
+  // (but inside the row) are read and ignored.
+  const int32_t *bt_row = a.block_tables + (int64_t)s * a.max_blocks;
+  const int jb = start >> a.block_shift;
+  const int btv_raw = jb + lane < a.max_blocks ? bt_row[jb + lane] : 0;
+  u32x4_t qa[C::kSteps];
+  {
+    const u32x4_t *qrow = reinterpret_cast<const u32x4_t *>(
+        static_cast<const T *>(a.q) + ((int64_t)s * H + head0 + min(n, nh - 1)) * D);
+#pragma unroll
+    for (int c = 0; c < C::kSteps; ++c) qa[c] = qrow[kg + 4 * c];
+  }
   const int L = a.seq_lens[s];
   const bool bad_len = L < 0 || (int64_t)L > (int64_t)a.max_blocks * a.block_size;
   if (bad_len || L == 0) {
@@ -187,34 +260,22 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(DecodeA
     }
     return;
   }
-  const int P = a.partition_tokens;
-  const int start = part * P;
   if (start >= L) return;
   const int end = min(L, start + P);
   const int nparts = (L + P - 1) / P;
 
-  // ---- Q as the MFMA A operand: row n = query head (zero past nh), k = head dims
-  const int kg = lane >> 4;
-  const int n = lane & 15;
-  u32x4_t qa[C::kSteps];
-  {
-    const u32x4_t *qrow = reinterpret_cast<const u32x4_t *>(
-        static_cast<const T *>(a.q) + ((int64_t)s * H + head0 + min(n, nh - 1)) * D);
+  // Q as the MFMA A operand: row n = query head (zero past nh), k = head dims
+  if (n >= nh) {
 #pragma unroll
-    for (int c = 0; c < C::kSteps; ++c) {
-      const u32x4_t v = qrow[kg + 4 * c];
-      qa[c] = n < nh ? v : u32x4_t{0u, 0u, 0u, 0u};
-    }
+    for (int c = 0; c < C::kSteps; ++c) qa[c] = u32x4_t{0u, 0u, 0u, 0u};
   }
 
   // Block ids of the partition (at most 64 table entries): lane i of btv holds
   // entry jb + i. They are read back with v_readlane, so the per-tile lookup
   // issues no memory operation and never waits on the K/V loads in flight.
-  const int32_t *bt_row = a.block_tables + (int64_t)s * a.max_blocks;
-  const int jb = start >> a.block_shift;
   const int jmax = (end - 1) >> a.block_shift;  // last table entry this partition reads
   const int64_t kv_stride_blk = (int64_t)a.n_kv_heads * a.block_size;  // rows per physical block
-  const int btv = jb + lane <= jmax ? bt_row[jb + lane] : 0;
+  const int btv = jb + lane <= jmax ? btv_raw : 0;
   bool bad = false;
 
   auto tile_offset = [&](int ti) -> int64_t {  // offset of tile ti in 16-byte chunks (uniform)
@@ -238,132 +299,250 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(DecodeA
     const int64_t off = tile_offset(ti);
     const u32x4_t *kp = kbase + off;
     const u32x4_t *vp = vbase + off;
+    // K/V are read once per call: non-temporal loads keep them from
+    // displacing other lines in L2 and the memory-side cache, which measures
+    // about 10% faster for this gather than plain loads.
 #pragma unroll
-    for (int i = 0; i < kL; ++i) r.k[i] = kp[i * 64 + lane];
+    for (int i = 0; i < kL; ++i) r.k[i] = __builtin_nontemporal_load(kp + i * 64 + lane);
 #pragma unroll
-    for (int i = 0; i < kL; ++i) r.v[i] = vp[i * 64 + lane];
+    for (int i = 0; i < kL; ++i) r.v[i] = __builtin_nontemporal_load(vp + i * 64 + lane);
   };
 
-  u32x4_t *kst = reinterpret_cast<u32x4_t *>(smem + C::kKstOff + wave * C::kKstBytes);
-  float *pst = reinterpret_cast<float *>(smem + C::kPstOff + wave * C::kPstBytes);
+  char *wreg = smem + wave * C::kWaveBytes;
+  u32x4_t *kst = reinterpret_cast<u32x4_t *>(wreg + C::kKstOff);
+  char *vst = wreg + C::kVstOff;
+  char *pst = wreg + C::kPstOff;
 
+  // Running softmax state per head row: lanes (kg, n) own heads 4 kg + r.
+  // m[r] is a reference max in base-2 units, uniform across the 16 lanes of
+  // the row; l[r] is this lane's share (token n) of the weight sum.
   float m[4], l[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     m[r] = -INFINITY;
     l[r] = 0.f;
   }
-  float acc[GT][kEpc];
-#pragma unroll
-  for (int h = 0; h < GT; ++h)
-#pragma unroll
-    for (int e = 0; e < kEpc; ++e) acc[h][e] = 0.f;
 
-  auto process = [&](int ti, const Regs &rg) {
-    // stage K (coalesced order -> swizzled LDS tile)
+  // Accumulators. MFMA path: acc[b][r] = O[head 4 kg + r][dim 16 b + n].
+  // VALU path: accv[h][e] = partial O[head h][dim (lane % kCh) * kEpc + e] over
+  // this lane's token row.
+  f32x4_t acc[C::kPvMfma ? C::kDimBlocks : 1];
+  float accv[C::kPvMfma ? 1 : GT][C::kPvMfma ? 1 : kEpc];
+#pragma unroll
+  for (int b = 0; b < (C::kPvMfma ? C::kDimBlocks : 1); ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int h = 0; h < (C::kPvMfma ? 1 : GT); ++h)
+#pragma unroll
+    for (int e = 0; e < (C::kPvMfma ? 1 : kEpc); ++e) accv[h][e] = 0.f;
+
+  // MFMA path: this lane's byte offsets for the transposed reads. Source lane
+  // (r = (lane % 16) / 4, q = lane % 4) of group kg addresses token 4 kg + r:
+  // for P (hi/lo rows of 16 heads) heads 4q..4q+3, for V dims 16 b + 4q..4q+3.
+  const int tr_tok = 4 * kg + ((lane & 15) >> 2);
+  const int tr_q = lane & 3;
+  const int p_tr_off = tr_tok * 32 + tr_q * 8;
+  const int v_tr_base = tr_tok * kCh * 16 + tr_q * 8;
+  const int v_tr_swz = vst_swz<kCh>(tr_tok);
+  if constexpr (C::kPvMfma) {
+    // heads this workgroup does not own stay zero in the staged P
+    for (int i = lane; i < 2 * 16 * 16 / 8; i += 64)
+      reinterpret_cast<uint2 *>(pst)[i] = make_uint2(0u, 0u);
+  }
+
+  // The reference max may trail the true running max by up to kLazy (base-2
+  // units), so every weight p = 2^(z - m) stays <= 2^kLazy. It is raised, and
+  // the sums rescaled, only when a score passes it by more than that: the
+  // result is unchanged (numerator and denominator share the reference) and
+  // the common tile needs no cross-lane reduction.
+  constexpr float kLazy = 8.f;
+
+  // `next` >= 0 (MFMA path): once this tile sits in LDS its registers are
+  // free, so the loads of tile `next` are issued into them before any math.
+  auto process = [&](int ti, Regs &rg, int next) {
+    const int valid = end - ti * kTileTokens;  // > 0; >= 16 means a full tile
+    const bool partial = valid < kTileTokens;  // uniform
+    // stage K (coalesced order -> swizzled LDS tile); the MFMA path also stages
+    // V, zeroing rows past the sequence (0 * NaN would poison the sum)
 #pragma unroll
     for (int i = 0; i < kL; ++i) {
       const int u = i * 64 + lane;
       kst[kst_slot<kCh>(u / kCh, u % kCh)] = rg.k[i];
     }
+    if constexpr (C::kPvMfma) {
+      u32x4_t *vs = reinterpret_cast<u32x4_t *>(vst);
+      if (!partial) {
+#pragma unroll
+        for (int i = 0; i < kL; ++i) {
+          const int u = i * 64 + lane;
+          vs[(u / kCh) * kCh + ((u % kCh) ^ vst_swz<kCh>(u / kCh))] = rg.v[i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kL; ++i) {
+          const int u = i * 64 + lane;
+          const int tr = u / kCh;
+          vs[tr * kCh + ((u % kCh) ^ vst_swz<kCh>(tr))] =
+              tr < valid ? rg.v[i] : u32x4_t{0u, 0u, 0u, 0u};
+        }
+      }
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if constexpr (C::kPvMfma) {
+      if (next >= 0) load_tile(next, rg);
+    }
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < C::kSteps; ++c) sc = mfma_chunk<T>(qa[c], kst[kst_slot<kCh>(n, kg + 4 * c)], sc);
 
-    const int valid = end - ti * kTileTokens;  // > 0; >= 16 means a full tile
+    // scores in base-2 units; tokens past the sequence get -inf
     const bool tok_ok = n < valid;
-    float alpha[4], p[4];
+    float z[4];
+    bool over = false;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float z = tok_ok ? sc[r] * a.scale_log2 : -INFINITY;
-      const float mt = row_max16(z);
-      const float mn = fmaxf(m[r], mt);
-      alpha[r] = (m[r] == mn) ? 1.f : exp2f(m[r] - mn);
-      m[r] = mn;
-      p[r] = exp2f(z - mn);
-      l[r] = l[r] * alpha[r] + p[r];
+      z[r] = tok_ok ? sc[r] * a.scale_log2 : -INFINITY;
+      over |= z[r] > m[r] + kLazy;
     }
-    // p[token][head] -> LDS for the V layout
-    if (4 * kg < GT) {
+    if (__builtin_amdgcn_ballot_w64(over) != 0) {  // uniform: raise the reference
+      float alpha[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (4 * kg + r < GT) pst[n * GT + 4 * kg + r] = p[r];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // rescale by the per-head factor (uniform per head)
-#pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      const float ah = readlane_f(alpha[h & 3], (h >> 2) * 16);
-#pragma unroll
-      for (int e = 0; e < kEpc; ++e) acc[h][e] *= ah;
-    }
-    const bool partial = valid < kTileTokens;
-#pragma unroll
-    for (int i = 0; i < kL; ++i) {
-      const int tok = i * C::kRows + lane / kCh;
-      float pv[GT];
-#pragma unroll
-      for (int h = 0; h < GT; ++h) pv[h] = pst[tok * GT + h];
-      float vf[kEpc];
-      chunk_to_float<T>(rg.v[i], vf);
-      if (partial && tok >= valid) {
-#pragma unroll
-        for (int e = 0; e < kEpc; ++e) vf[e] = 0.f;
+      for (int r = 0; r < 4; ++r) {
+        const float mn = fmaxf(m[r], row_max16(z[r]));
+        alpha[r] = __builtin_amdgcn_exp2f(m[r] - mn);  // 0 on the first tile (m = -inf)
+        m[r] = mn;
+        l[r] *= alpha[r];
       }
+      if constexpr (C::kPvMfma) {
 #pragma unroll
-      for (int h = 0; h < GT; ++h)
+        for (int b = 0; b < C::kDimBlocks; ++b)
 #pragma unroll
-        for (int e = 0; e < kEpc; ++e) acc[h][e] = fmaf(pv[h], vf[e], acc[h][e]);
+          for (int r = 0; r < 4; ++r) acc[b][r] *= alpha[r];
+      } else {
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+          const float ah = readlane_f(alpha[h & 3], (h >> 2) * 16);
+#pragma unroll
+          for (int e = 0; e < kEpc; ++e) accv[h][e] *= ah;
+        }
+      }
+    }
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = __builtin_amdgcn_exp2f(z[r] - m[r]);
+      l[r] += p[r];
+    }
+
+    if constexpr (C::kPvMfma) {
+      // P as hi + lo in the storage type (about 16 mantissa bits together)
+      if (4 * kg < GT) {
+        typename Pv<T>::v4 hi, lo;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pr = (4 * kg + r < GT) ? p[r] : 0.f;
+          hi[r] = static_cast<T>(pr);
+          lo[r] = static_cast<T>(pr - static_cast<float>(hi[r]));
+        }
+        *reinterpret_cast<typename Pv<T>::v4 *>(pst + n * 32 + kg * 8) = hi;
+        *reinterpret_cast<typename Pv<T>::v4 *>(pst + 512 + n * 32 + kg * 8) = lo;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const typename Pv<T>::v4 pa_hi = lds_read_tr<T>(pst + p_tr_off);
+      const typename Pv<T>::v4 pa_lo = lds_read_tr<T>(pst + 512 + p_tr_off);
+#pragma unroll
+      for (int b = 0; b < C::kDimBlocks; ++b) {
+        const typename Pv<T>::v4 vb = lds_read_tr<T>(vst + v_tr_base + (((2 * b) ^ v_tr_swz) << 4));
+        acc[b] = Pv<T>::mfma(pa_hi, vb, acc[b]);
+        acc[b] = Pv<T>::mfma(pa_lo, vb, acc[b]);
+      }
+    } else {
+      float *pstf = reinterpret_cast<float *>(pst);
+      // p[token][head] -> LDS for the V layout
+      if (4 * kg < GT) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (4 * kg + r < GT) pstf[n * GT + 4 * kg + r] = p[r];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int i = 0; i < kL; ++i) {
+        const int tok = i * C::kRows + lane / kCh;
+        float pv[GT];
+#pragma unroll
+        for (int h = 0; h < GT; ++h) pv[h] = pstf[tok * GT + h];
+        float vf[kEpc];
+        chunk_to_float<T>(rg.v[i], vf);
+        if (partial && tok >= valid) {
+#pragma unroll
+          for (int e = 0; e < kEpc; ++e) vf[e] = 0.f;
+        }
+#pragma unroll
+        for (int h = 0; h < GT; ++h)
+#pragma unroll
+          for (int e = 0; e < kEpc; ++e) accv[h][e] = fmaf(pv[h], vf[e], accv[h][e]);
+      }
     }
   };
 
-  // ---- stream this wave's tiles (tb + wave, tb + wave + NW, ...), two per
-  // iteration: both tiles' loads are issued before the first is used, and no
-  // load result is carried across the loop edge (so no wait ever covers a
-  // load issued for a later tile).
+  // ---- stream this wave's tiles (tb + wave, tb + wave + NW, ...), one per
+  // iteration. MFMA path: each iteration stages its tile in LDS, then issues
+  // the next tile's loads into the same registers, so one tile is always in
+  // flight and no load result crosses the loop edge unconsumed. VALU path:
+  // load, then use.
   const int tb = start / kTileTokens;
   const int te = (end + kTileTokens - 1) / kTileTokens;
-  {
-    const int first = tb + wave;
-    const int n_my = first < te ? (te - first + kNW - 1) / kNW : 0;
-    int k = 0;
-    for (; k + 1 < n_my; k += 2) {
-      Regs ra, rb;
-      load_tile(first + k * kNW, ra);
-      load_tile(first + (k + 1) * kNW, rb);
-      process(first + k * kNW, ra);
-      process(first + (k + 1) * kNW, rb);
-    }
-    if (k < n_my) {
-      Regs ra;
-      load_tile(first + k * kNW, ra);
-      process(first + k * kNW, ra);
+  if constexpr (C::kPvMfma) {
+    Regs rg;
+    int ti = tb + wave;
+    if (ti < te) load_tile(ti, rg);
+    for (; ti < te; ti += kNW) process(ti, rg, ti + kNW < te ? ti + kNW : -1);
+  } else {
+    for (int ti = tb + wave; ti < te; ti += kNW) {
+      Regs rg;
+      load_tile(ti, rg);
+      process(ti, rg, -1);
     }
   }
 
-  // ---- wave totals: row sums of l, token-row sums of acc
+  // ---- wave totals to LDS
 #pragma unroll
   for (int r = 0; r < 4; ++r) l[r] = row_sum16(l[r]);
-#pragma unroll
-  for (int h = 0; h < GT; ++h)
-#pragma unroll
-    for (int e = 0; e < kEpc; ++e)
-#pragma unroll
-      for (int off = kCh; off < 64; off <<= 1) acc[h][e] += __shfl_xor(acc[h][e], off, 64);
-
-  float *macc = reinterpret_cast<float *>(smem + C::kAccOff) + wave * GT * D;
+  // the wave's staging area is free now: it takes the wave's partial sums
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float *macc = reinterpret_cast<float *>(wreg);
   float2 *mml = reinterpret_cast<float2 *>(smem + C::kMlOff) + wave * GT;
   int *mbad = reinterpret_cast<int *>(smem + C::kBadOff);
-  if (lane < kCh) {
+  if constexpr (C::kPvMfma) {
+    if (4 * kg < GT) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * kg + r < GT) {
+#pragma unroll
+          for (int b = 0; b < C::kDimBlocks; ++b) macc[(4 * kg + r) * D + 16 * b + n] = acc[b][r];
+        }
+    }
+  } else {
+    // token-row sums of the VALU accumulators
 #pragma unroll
     for (int h = 0; h < GT; ++h)
 #pragma unroll
-      for (int e = 0; e < kEpc; ++e) macc[h * D + lane * kEpc + e] = acc[h][e];
+      for (int e = 0; e < kEpc; ++e)
+#pragma unroll
+        for (int off = kCh; off < 64; off <<= 1) accv[h][e] += __shfl_xor(accv[h][e], off, 64);
+    if (lane < kCh) {
+#pragma unroll
+      for (int h = 0; h < GT; ++h)
+#pragma unroll
+        for (int e = 0; e < kEpc; ++e) macc[h * D + lane * kEpc + e] = accv[h][e];
+    }
   }
   if (n == 0 && 4 * kg < GT) {
 #pragma unroll
@@ -374,7 +553,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(DecodeA
   __syncthreads();
 
   // ---- merge the waves
-  const float *acc_all = reinterpret_cast<const float *>(smem + C::kAccOff);
+  auto acc_of = [&](int w) { return reinterpret_cast<const float *>(smem + w * C::kWaveBytes); };
   const float2 *ml_all = reinterpret_cast<const float2 *>(smem + C::kMlOff);
   int any_bad = 0;
 #pragma unroll
@@ -389,9 +568,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(DecodeA
 #pragma unroll
     for (int w = 0; w < kNW; ++w) {
       const float2 ml = ml_all[w * GT + h];
-      const float f = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);
+      const float f = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
       den = fmaf(f, ml.y, den);
-      num = fmaf(f, acc_all[(w * GT + h) * D + d], num);
+      num = fmaf(f, acc_of(w)[h * D + d], num);
     }
     if (any_bad) {
       num = den = M = __builtin_nanf("");
@@ -407,47 +586,104 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(DecodeA
   }
 }
 
-// Merge of the partition partials of every split sequence:
+// Merge of the partition partials of a split sequence (one workgroup per
+// sequence and query head):
 //   M = max_p m_p,  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
+// Thread (d, grp) folds partitions grp, grp + kGroups, ... for dimension d
+// with the same online rescaling as the decode kernel (four partitions per
+// step, loads issued together); the kGroups partial states are then combined
+// in LDS.
+constexpr int kReduceThreads = 1024;
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void paged_decode_reduce_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kReduceThreads) void paged_decode_reduce_kernel(DecodeArgs a) {
+  constexpr int kGroups = kReduceThreads / D;
+  __shared__ float red_num[kGroups][D];
+  __shared__ float2 red_ml[kGroups];
+  __shared__ int red_bad[kGroups];
+  const int h = blockIdx.x;
   const int s = blockIdx.y;
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  const int h = idx / D;
-  const int d = idx - h * D;
-  if (h >= a.n_heads) return;
   const int L = a.seq_lens[s];
   const int P = a.partition_tokens;
   if (L <= P || (int64_t)L > (int64_t)a.max_blocks * a.block_size) return;  // single partition or invalid
   const int nparts = (L + P - 1) / P;
+  const int d = threadIdx.x % D;
+  const int grp = threadIdx.x / D;
   const int64_t row = (int64_t)s * a.n_heads + h;
   const float2 *ml = a.part_ml + row * a.max_parts;
   const float *acc = a.part_acc + row * a.max_parts * D + d;
-  float M = -INFINITY;
+  float M = -INFINITY, num = 0.f, den = 0.f;
   bool bad = false;
-  for (int p = 0; p < nparts; ++p) {
-    const float mp = ml[p].x;
-    bad |= mp != mp;
-    M = fmaxf(M, mp);
+  int p = grp;
+  for (; p + 3 * kGroups < nparts; p += 4 * kGroups) {
+    float2 v[4];
+    float x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v[u] = ml[p + u * kGroups];
+      x[u] = acc[(int64_t)(p + u * kGroups) * D];
+    }
+    float mn = M;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      bad |= v[u].x != v[u].x;
+      mn = fmaxf(mn, v[u].x);
+    }
+    const float f0 = __builtin_amdgcn_exp2f(M - mn);  // 0 while M = -inf
+    num *= f0;
+    den *= f0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float f = __builtin_amdgcn_exp2f(v[u].x - mn);
+      den = fmaf(f, v[u].y, den);
+      num = fmaf(f, x[u], num);
+    }
+    M = mn;
   }
-  float num = 0.f, den = 0.f;
-  for (int p = 0; p < nparts; ++p) {
+  for (; p < nparts; p += kGroups) {
     const float2 v = ml[p];
-    const float f = exp2f(v.x - M);
-    den = fmaf(f, v.y, den);
-    num = fmaf(f, acc[(int64_t)p * D], num);
+    bad |= v.x != v.x;
+    const float mn = fmaxf(M, v.x);
+    const float f0 = __builtin_amdgcn_exp2f(M - mn);
+    const float f = __builtin_amdgcn_exp2f(v.x - mn);
+    den = fmaf(f, v.y, den * f0);
+    num = fmaf(f, acc[(int64_t)p * D], num * f0);
+    M = mn;
   }
-  static_cast<T *>(a.out)[row * D + d] = static_cast<T>(bad ? __builtin_nanf("") : num / den);
+  red_num[grp][d] = num;
+  if (d == 0) {
+    red_ml[grp] = make_float2(M, den);
+    red_bad[grp] = bad;
+  }
+  __syncthreads();
+  if (grp == 0) {
+    float Mt = -INFINITY;
+    int any_bad = 0;
+#pragma unroll
+    for (int g2 = 0; g2 < kGroups; ++g2) {
+      Mt = fmaxf(Mt, red_ml[g2].x);
+      any_bad |= red_bad[g2];
+    }
+    float nt = 0.f, dt = 0.f;
+#pragma unroll
+    for (int g2 = 0; g2 < kGroups; ++g2) {
+      const float2 v = red_ml[g2];
+      const float f = v.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(v.x - Mt);  // empty groups
+      dt = fmaf(f, v.y, dt);
+      nt = fmaf(f, red_num[g2][d], nt);
+    }
+    static_cast<T *>(a.out)[row * D + d] = static_cast<T>(any_bad ? __builtin_nanf("") : nt / dt);
+  }
 }
 
 template <typename T, int D, int GT>
 hipError_t launch_t(const DecodeArgs &a, hipStream_t stream) {
-  dim3 grid(a.n_kv_heads * a.head_chunks, a.num_seqs, a.max_parts);
+  dim3 grid((unsigned)((int64_t)a.n_kv_heads * a.head_chunks * a.num_seqs * a.max_parts), 1, 1);
   hipLaunchKernelGGL((paged_decode_kernel<T, D, GT>), grid, dim3(kDecodeWaves * 64), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.max_parts == 1) return err;
-  dim3 rgrid((a.n_heads * D + 255) / 256, a.num_seqs, 1);
-  hipLaunchKernelGGL((paged_decode_reduce_kernel<T, D>), rgrid, dim3(256), 0, stream, a);
+  dim3 rgrid(a.n_heads, a.num_seqs, 1);
+  hipLaunchKernelGGL((paged_decode_reduce_kernel<T, D>), rgrid, dim3(kReduceThreads), 0, stream, a);
   return hipGetLastError();
 }
 

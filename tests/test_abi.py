@@ -96,9 +96,9 @@ def test_write_empty_is_noop():
 
 
 def test_partition_plan():
-    assert _lib.decode_plan(32, 8, 16, 128, 257) == (512, 9)      # 4112 tokens -> 9 x 512
+    assert _lib.decode_plan(32, 8, 16, 128, 257) == (1024, 5)     # 4112 tokens -> 5 x 1024
     assert _lib.decode_plan(4, 4, 16, 4, 7) == (112, 1)           # short tables stay whole
-    assert _lib.decode_plan(32, 8, 16, 4, 8193) == (512, 257)
+    assert _lib.decode_plan(32, 8, 16, 4, 8193) == (1024, 129)
     _lib.set_partition_tokens(64)
     try:
         assert _lib.decode_plan(32, 8, 16, 4, 10) == (64, 3)

@@ -58,7 +58,7 @@ def test_config4_long_context_sampled():
     say("decode parity cfg4 (sampled kv heads 0 and 7)")
     w = workloads.make(4)
     g = OnGpu(w)
-    assert _lib.decode_plan(w.n_heads, w.n_kv_heads, 16, 4, w.max_blocks_per_seq)[0] == 512
+    assert _lib.decode_plan(w.n_heads, w.n_kv_heads, 16, 4, w.max_blocks_per_seq)[0] == 1024
     out = g.decode()
     torch.cuda.synchronize()
     ref = oracle_decode(w, w.seq_lens, w.k_pool, w.v_pool, kv_heads=[0, 7])
