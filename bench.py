@@ -31,12 +31,30 @@ import torch
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from paged_kv_cache_260_amd import _lib, accounting, workloads  # noqa: E402
+from paged_kv_cache_260_amd import _lib, accounting, profiling, workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MALL_BYTES = 256 * 2 ** 20     # memory-side (Infinity) cache
 METRIC = "paged decode effective HBM GB/s (% of MI355X peak) + us/batch, GQA bs=128"
 DTYPE_NAMES = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+# profile summaries under profiles/, by workload
+PROFILE_NAMES = {1: "paged_decode_tiny_f32_b4", 2: "paged_decode_mha_bf16_b64",
+                 3: "paged_decode_gqa_bf16_b128", 4: "paged_decode_long_bf16_b4",
+                 5: "paged_decode_prefix_f16_b64"}
+
+
+def measured_traffic(cfg):
+    """HBM bytes per decode call from the committed counter summary, or None when
+    there is none or the decode source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", PROFILE_NAMES[cfg] + "_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("decode_source_hash") != profiling.source_hash() or "traffic_bytes_per_call" not in rec:
+        return None
+    return int(rec["traffic_bytes_per_call"])
 
 
 def log(msg):
@@ -215,7 +233,7 @@ def main():
         "step_bytes": int(step_bytes),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic(args.config),
                      "kernel": "paged_attn_decode call (decode kernel"
                                + (" + partition merge kernel)" if nparts > 1 else ")"),
                      "algorithmic_bytes": int(dec_bytes)},
