@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 from paged_kv_cache_260_amd import _lib, accounting, profiling, workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FUSED_MERGE_PARTS = 8          # partition counts merged inside the decode kernel
 MALL_BYTES = 256 * 2 ** 20     # memory-side (Infinity) cache
 METRIC = "paged decode effective HBM GB/s (% of MI355X peak) + us/batch, GQA bs=128"
 DTYPE_NAMES = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
@@ -235,7 +236,9 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(args.config),
                      "kernel": "paged_attn_decode call (decode kernel"
-                               + (" + partition merge kernel)" if nparts > 1 else ")"),
+                               + (")" if nparts == 1 else
+                                  ", partitions merged in-kernel)" if nparts <= FUSED_MERGE_PARTS else
+                                  " + partition merge kernel)"),
                      "algorithmic_bytes": int(dec_bytes)},
         "wall_ms_per_step": round(wall * 1e3 / K, 5),
     }

@@ -106,6 +106,39 @@ int get_workspace(hipStream_t stream, size_t bytes, void **out) {
   return PKV_OK;
 }
 
+// Arrival counters of the in-kernel partition merge, one set per (device,
+// stream): zeroed when allocated, and every call leaves them at zero again.
+std::map<std::pair<int, hipStream_t>, Workspace> g_arrivals;
+
+int get_arrivals(hipStream_t stream, int64_t count, int32_t **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  Workspace &ws = g_arrivals[{dev, stream}];
+  const size_t bytes = (size_t)count * sizeof(int32_t);
+  if (ws.bytes < bytes) {
+    if (ws.ptr) {
+      e = hipStreamSynchronize(stream);
+      if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+      hipFree(ws.ptr);
+      ws.ptr = nullptr;
+      ws.bytes = 0;
+    }
+    const size_t grow = (bytes + bytes / 2 + 255) & ~(size_t)255;
+    e = hipMalloc(&ws.ptr, grow);
+    if (e != hipSuccess) {
+      ws.ptr = nullptr;
+      return hip_fail(e, "hipMalloc (decode arrival counters)");
+    }
+    e = pkv::launch_zero_i32(static_cast<int32_t *>(ws.ptr), (int64_t)(grow / sizeof(int32_t)), stream);
+    if (e != hipSuccess) return hip_fail(e, "clearing decode arrival counters");
+    ws.bytes = grow;
+  }
+  *out = static_cast<int32_t *>(ws.ptr);
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -200,6 +233,10 @@ int pkv_paged_attn_decode(void *out, const void *q, const void *k_pool, const vo
     if (rc != PKV_OK) return rc;
     a.part_acc = static_cast<float *>(ws);
     a.part_ml = reinterpret_cast<float2 *>(static_cast<char *>(ws) + acc_bytes);
+    if (a.max_parts <= pkv::kFusedMergeParts) {
+      rc = get_arrivals(st, (int64_t)num_seqs * n_kv_heads * a.head_chunks, &a.arrivals);
+      if (rc != PKV_OK) return rc;
+    }
   }
   hipError_t e = pkv::launch_decode(static_cast<pkv::DType>(dtype), head_dim, a, st);
   if (e != hipSuccess) return hip_fail(e, "paged decode launch");
@@ -244,18 +281,20 @@ int pkv_kv_cache_write(void *k_pool, void *v_pool, const void *k_new, const void
 int pkv_release_workspace(void) {
   std::lock_guard<std::mutex> lock(g_ws_mu);
   int rc = PKV_OK;
-  for (auto &kv : g_ws) {
-    if (!kv.second.ptr) continue;
-    int prev = 0;
-    hipGetDevice(&prev);
-    hipSetDevice(kv.first.first);
-    hipError_t e = hipStreamSynchronize(kv.first.second);
-    if (e == hipSuccess) e = hipFree(kv.second.ptr);
-    hipSetDevice(prev);
-    if (e != hipSuccess) rc = hip_fail(e, "releasing workspace");
-    kv.second = Workspace{};
+  for (auto *m : {&g_ws, &g_arrivals}) {
+    for (auto &kv : *m) {
+      if (!kv.second.ptr) continue;
+      int prev = 0;
+      hipGetDevice(&prev);
+      hipSetDevice(kv.first.first);
+      hipError_t e = hipStreamSynchronize(kv.first.second);
+      if (e == hipSuccess) e = hipFree(kv.second.ptr);
+      hipSetDevice(prev);
+      if (e != hipSuccess) rc = hip_fail(e, "releasing workspace");
+      kv.second = Workspace{};
+    }
+    m->clear();
   }
-  g_ws.clear();
   return rc == PKV_OK ? ok() : rc;
 }
 

@@ -20,21 +20,25 @@ __global__ __launch_bounds__(kWriteThreads) void kv_cache_write_kernel(CacheWrit
   uint4 *kp = static_cast<uint4 *>(a.k_pool);
   uint4 *vp = static_cast<uint4 *>(a.v_pool);
   for (int t = blockIdx.x; t < a.num_tokens; t += gridDim.x) {
-    const int64_t slot = a.slot_mapping[t];
-    if (slot < 0 || slot >= a.num_slots) continue;
-    const int64_t blk = slot / a.block_size;
-    const int64_t off = slot - blk * a.block_size;
+    // The rows are read before the slot is known (both loads in flight at
+    // once); only the stores depend on it.
     for (int u = threadIdx.x; u < 2 * units; u += kWriteThreads) {
       const bool is_v = u >= units;
       const int uu = is_v ? u - units : u;
+      const int64_t src = (int64_t)t * units + uu;
+      int32_t slot32 = a.slot_mapping[t];
+      uint4 val = is_v ? vn[src] : kn[src];
+      // an empty asm that consumes both values: the compiler may not sink the
+      // row load below the slot test, so one wait covers both loads
+      asm volatile("" : "+v"(slot32), "+v"(val.x), "+v"(val.y), "+v"(val.z), "+v"(val.w));
+      const int64_t slot = slot32;
+      if (slot < 0 || slot >= a.num_slots) continue;
+      const int64_t blk = slot / a.block_size;
+      const int64_t off = slot - blk * a.block_size;
       const int head = uu / a.row_chunks;
       const int c = uu - head * a.row_chunks;
-      const int64_t src = (int64_t)t * units + uu;
       const int64_t dst = ((blk * a.n_kv_heads + head) * a.block_size + off) * a.row_chunks + c;
-      if (is_v)
-        vp[dst] = vn[src];
-      else
-        kp[dst] = kn[src];
+      (is_v ? vp : kp)[dst] = val;
     }
   }
 }

@@ -9,34 +9,38 @@
 // "FlashAttention": tiling plus online softmax, exact). Query heads that share
 // a KV head (GQA/MQA, ICML-tutorial notes page) are processed together so each
 // K/V tile is read from HBM once per group. Long sequences are split along the
-// sequence (FlashDecoding, same tutorial page, kernel-optimisation part) and
-// the partial results are merged by a second kernel.
+// sequence into partitions (FlashDecoding, same tutorial page, kernel-
+// optimisation part) whose partial results are merged by the last partition
+// to finish, or by a separate merge kernel when a table allows more than
+// kFusedMergeParts partitions.
 //
-// Work decomposition (one workgroup = 4 waves):
-//   blockIdx.x = KV head x query-head chunk, blockIdx.y = sequence,
-//   blockIdx.z = partition of `partition_tokens` tokens.
-//   Inside a workgroup the partition's 16-token tiles go round-robin to the
-//   waves; each wave keeps its own running max / sum / accumulator and the
-//   four are merged through LDS at the end.
+// Work decomposition: one workgroup (4 waves) per work item = (KV head x
+// query-head chunk, sequence, partition), items handed out longest first
+// (make_plan / locate_item). Inside a workgroup the partition's 16-token
+// tiles go round-robin to the waves; each wave keeps its own running max /
+// sum / accumulator and the four are merged through LDS at the end.
 //
 // Per 16-token tile, per wave:
-//   1. K and V tiles (16 x head_dim each) are fetched with fully coalesced
-//      16-byte loads into registers, one tile ahead of the one being used
-//      (register double buffering).
-//   2. K goes to a wave-private LDS tile (XOR-swizzled 16-byte chunks, bank
-//      conflict free both ways) and is read back in the MFMA B-operand layout:
-//      lane (kg = lane/16, n = lane%16) holds token n, chunk kg + 4c.
+//   1. K and V tiles (16 x head_dim each) arrive by fully coalesced 16-byte
+//      non-temporal loads into registers, issued one tile ahead.
+//   2. Both go to wave-private LDS tiles (XOR-swizzled 16-byte chunks, bank
+//      conflict free for the writes and the operand reads); the registers
+//      then take the next tile's loads.
 //   3. Scores S[head][token] = Q (heads x D, rows padded to 16) * K^T come out
 //      of v_mfma_f32_16x16x32_{bf16,f16} (16x16x4 for fp32): lane (kg, n)
 //      receives heads 4kg..4kg+3 of token n.
-//   4. Online softmax in base 2 (scale * log2 e folded into one multiply):
-//      the tile max per head is a 16-lane DPP row reduction; p = exp2(z - m).
-//   5. p goes through LDS to the V layout, where each lane owns one 16-byte
-//      chunk of head dims and a quarter of the tokens; acc += p * v in fp32 on
-//      the VALU, no cross-lane work inside the loop.
+//   4. Online softmax in base 2 (scale * log2 e folded into one multiply)
+//      against a reference max that is raised only when a score passes it by
+//      more than 8 (so every weight stays <= 2^8); only then are rows reduced
+//      with DPP and the sums rescaled.
+//   5. 16-bit storage: P (as hi + lo halves) and the V tile are read back
+//      transposed with ds_read_b64_tr_b16 and multiplied on
+//      v_mfma_f32_16x16x16; fp32 storage accumulates P * V on the VALU.
 #include "kernels.h"
 
 #include <math.h>
+
+#include <atomic>
 
 namespace pkv {
 namespace {
@@ -181,7 +185,8 @@ template <typename T, int D, int GT> struct Cfg {
   static constexpr int kPstOff = kKstBytes + kVstBytes;
   static constexpr int kMlOff = kNW * kWaveBytes;        // workgroup-wide
   static constexpr int kBadOff = kMlOff + kNW * GT * 8;
-  static constexpr int kSmem = kBadOff + kNW * 4;
+  static constexpr int kFlagOff = kBadOff + kNW * 4;
+  static constexpr int kSmem = kFlagOff + 4;
   static_assert(kCh % 4 == 0 && 64 % kCh == 0, "head_dim must give 8, 16 or 32 chunks");
   static_assert(!kPvMfma || kCh == 8 || kCh == 16, "MFMA P*V path: 8 or 16 chunks per row");
   static_assert(GT >= 1 && GT <= 16, "head tile");
@@ -201,31 +206,120 @@ template <int kCh> __device__ __forceinline__ int vst_swz(int tr) {
   return kCh >= 16 ? (2 * tr) & 15 : 2 * ((tr >> 1) & 3);
 }
 
+// Longest-first item order for batches of up to kCompactSeqs sequences.
+// A sequence of L tokens has n = ceil(L / P) partitions: n - 1 full ones and
+// a last one of L - (n - 1) P tokens. Item j of a unit is, in this order:
+//   1. the full partitions of all sequences (sequence-major), then
+//   2. the last partitions, in kRemBuckets buckets of decreasing length
+//      (sequence order within a bucket); zero-length and invalid sequences
+//      come last (their one item writes the zero or NaN row).
+// Each wave derives the order from the lengths by itself (wave-wide scans and
+// ballots over 64-sequence chunks held in registers), so no workgroup-wide
+// synchronisation is needed.
+constexpr int kCompactSeqs = 256;
+constexpr int kCompactChunks = kCompactSeqs / 64;
+constexpr int kRemBuckets = 8;
+
+struct ItemPlan {
+  int fb[kCompactChunks];  // per lane: (full partitions << 4) | bucket, bucket 15 = no sequence
+  int full_items;          // full partitions of the batch (uniform)
+  int items;               // all items of one unit (uniform)
+};
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ void make_plan(const DecodeArgs &a, ItemPlan &pl) {
+  const int lane = threadIdx.x & 63;
+  const int B = a.num_seqs;
+  const int P = a.partition_tokens;
+  const int64_t max_tok = (int64_t)a.max_blocks * a.block_size;
+  int full_sum = 0;
+#pragma unroll
+  for (int c = 0; c < kCompactChunks; ++c) {
+    pl.fb[c] = 15;
+    const int sq = c * 64 + lane;
+    if (sq < B) {
+      const int L = a.seq_lens[sq];
+      const bool ok = L > 0 && (int64_t)L <= max_tok;
+      const int full = ok ? (L - 1) / P : 0;
+      const int rem = L - full * P;  // 1 .. P when ok
+      pl.fb[c] = (full << 4) | (ok ? (int)(((int64_t)(P - rem) * kRemBuckets) / P) : kRemBuckets);
+      full_sum += full;
+    }
+  }
+  pl.full_items = __builtin_amdgcn_readlane(wave_incl_scan(full_sum, lane), 63);
+  pl.items = pl.full_items + B;
+}
+
+// Item j (< pl.items) of the order above -> (sequence, partition), uniform.
+// Written without early exits: every chunk and bucket is visited, the match
+// recorded once (an early return here made the compiler keep far more
+// registers live through the decode loop).
+__device__ __forceinline__ void locate_item(const ItemPlan &pl, int B, int j, int &s_out, int &p_out) {
+  const int lane = threadIdx.x & 63;
+  int s_res = 0, p_res = 0;
+  bool found = false;
+  if (j < pl.full_items) {
+    int base = 0;
+#pragma unroll
+    for (int c = 0; c < kCompactChunks; ++c) {
+      if (c * 64 < B) {
+        const int x = wave_incl_scan(pl.fb[c] >> 4, lane);
+        const int tot = __builtin_amdgcn_readlane(x, 63);
+        if (!found && j < base + tot) {
+          const int sl = __builtin_ctzll(__builtin_amdgcn_ballot_w64(base + x > j));
+          s_res = c * 64 + sl;
+          p_res = j - (base + __builtin_amdgcn_readlane(x, sl) - (__builtin_amdgcn_readlane(pl.fb[c], sl) >> 4));
+          found = true;
+        }
+        base += tot;
+      }
+    }
+  } else {
+    int jj = j - pl.full_items;
+    for (int b = 0; b <= kRemBuckets; ++b) {
+#pragma unroll
+      for (int c = 0; c < kCompactChunks; ++c) {
+        if (c * 64 < B) {
+          const bool in = (pl.fb[c] & 15) == b;
+          const unsigned long long m = __builtin_amdgcn_ballot_w64(in);
+          const int pc = __popcll(m);
+          if (!found && jj < pc) {
+            const int below =
+                __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+            const int sl = __builtin_ctzll(__builtin_amdgcn_ballot_w64(in && below == jj));
+            s_res = c * 64 + sl;
+            p_res = __builtin_amdgcn_readlane(pl.fb[c], sl) >> 4;
+            found = true;
+          }
+          jj -= pc;
+        }
+      }
+    }
+  }
+  s_out = s_res;
+  p_out = p_res;
+}
+
+// One work item: query heads [hc GT, hc GT + GT) of KV head g (unit = g x
+// head chunk hc) over tokens [part P, part P + P) of sequence s.
 template <typename T, int D, int GT>
-__global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int tid, int unit, int s, int part) {
   using C = Cfg<T, D, GT>;
   constexpr int kL = C::kLoads;
   constexpr int kCh = C::kCh;
   constexpr int kEpc = C::kEpc;
   constexpr int kNW = C::kNW;
-  __shared__ __attribute__((aligned(16))) char smem[C::kSmem];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // Work item of this workgroup. The hardware deals workgroup i to XCD i % 8
-  // and, within it, to shader engine (i / 8) % 4, each engine filling its own
-  // CUs. Order: unit (KV head x query-head chunk) fastest, so the sequences a
-  // KV head serves stay on one XCD and its L2 (shared-prefix blocks are read
-  // together); then sequence, then partition, so the empty tail partitions of
-  // short sequences come last; and the sequence index rotated by the
-  // partition index, so one long sequence's partitions cycle through all
-  // engines instead of piling onto one.
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int units = a.n_kv_heads * a.head_chunks;
-  const int64_t lin = blockIdx.x;
-  const int unit = (int)(lin % units);
-  const int64_t r = lin / units;
-  const int part = (int)(r / a.num_seqs);
-  const int s = (int)((r % a.num_seqs + a.num_seqs - part % a.num_seqs) % a.num_seqs);
   const int g = unit / a.head_chunks;
   const int hc = unit - g * a.head_chunks;
   const int H = a.n_heads;
@@ -255,7 +349,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(DecodeA
   if (bad_len || L == 0) {
     if (part == 0) {
       const float v = bad_len ? __builtin_nanf("") : 0.f;
-      for (int i = threadIdx.x; i < nh * D; i += kNW * 64)
+      for (int i = tid; i < nh * D; i += kNW * 64)
         out[((int64_t)s * H + head0) * D + i] = static_cast<T>(v);
     }
     return;
@@ -552,13 +646,22 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(DecodeA
   if (lane == 0) mbad[wave] = bad ? 1 : 0;
   __syncthreads();
 
-  // ---- merge the waves
+  // ---- merge the waves: thread t owns output elements t, t + 256, ... of the
+  // nh x D block (head-major); kPer of them at most
+  constexpr int kPer = (GT * D + kNW * 64 - 1) / (kNW * 64);
   auto acc_of = [&](int w) { return reinterpret_cast<const float *>(smem + w * C::kWaveBytes); };
   const float2 *ml_all = reinterpret_cast<const float2 *>(smem + C::kMlOff);
   int any_bad = 0;
 #pragma unroll
   for (int w = 0; w < kNW; ++w) any_bad |= mbad[w];
-  for (int idx = threadIdx.x; idx < nh * D; idx += kNW * 64) {
+  const bool fused = nparts > 1 && a.arrivals != nullptr;
+  float rM[kPer], rnum[kPer], rden[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int idx = tid + k * kNW * 64;
+    rM[k] = -INFINITY;
+    rnum[k] = rden[k] = 0.f;
+    if (idx >= nh * D) continue;
     const int h = idx / D;
     const int d = idx - h * D;
     float M = -INFINITY;
@@ -575,14 +678,140 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_kernel(DecodeA
     if (any_bad) {
       num = den = M = __builtin_nanf("");
     }
+    rM[k] = M;
+    rnum[k] = num;
+    rden[k] = den;
     const int64_t row = (int64_t)s * H + head0 + h;
     if (nparts == 1) {
       out[row * D + d] = static_cast<T>(num / den);
     } else {
       const int64_t pi = row * a.max_parts + part;
-      a.part_acc[pi * D + d] = num;
-      if (d == 0) a.part_ml[pi] = make_float2(M, den);
+      if (!fused) {
+        a.part_acc[pi * D + d] = num;
+        if (d == 0) a.part_ml[pi] = make_float2(M, den);
+      } else {
+        // agent-scope stores: written through to memory, where the last
+        // partition of the sequence (possibly on another XCD) reads them
+        __hip_atomic_store(a.part_acc + pi * D + d, num, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (d == 0)
+          __hip_atomic_store(reinterpret_cast<unsigned long long *>(a.part_ml + pi),
+                             __builtin_bit_cast(unsigned long long, make_float2(M, den)),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
+  }
+  if (!fused) return;
+
+  // ---- split sequence, merged by the last of its partitions to finish.
+  // Every partition's partial stores are complete (waited for) before the
+  // workgroup's arrival is counted, so the partition whose increment returns
+  // nparts - 1 finds all the other partials in memory; it reads them with
+  // agent-scope loads (never stale lines of its XCD's L2), resets the counter
+  // for the next call and writes the merged rows:
+  //   M = max_p m_p,  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int *flag = reinterpret_cast<int *>(smem + C::kFlagOff);
+  if (tid == 0) {
+    int32_t *cnt = a.arrivals + (int64_t)s * units + unit;
+    const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = prev == nparts - 1;
+    if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = last;
+  }
+  __syncthreads();
+  if (!*flag) return;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int idx = tid + k * kNW * 64;
+    if (idx >= nh * D) continue;
+    const int h = idx / D;
+    const int d = idx - h * D;
+    const int64_t row = (int64_t)s * H + head0 + h;
+    float2 oml[kFusedMergeParts];
+    float ox[kFusedMergeParts];
+#pragma unroll
+    for (int p = 0; p < kFusedMergeParts; ++p) {
+      oml[p] = make_float2(-INFINITY, 0.f);
+      ox[p] = 0.f;
+      if (p < nparts && p != part) {
+        const int64_t pi = row * a.max_parts + p;
+        oml[p] = __builtin_bit_cast(
+            float2, __hip_atomic_load(reinterpret_cast<unsigned long long *>(a.part_ml + pi),
+                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        ox[p] = __hip_atomic_load(a.part_acc + pi * D + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    float M = rM[k];
+    bool bad = M != M;
+#pragma unroll
+    for (int p = 0; p < kFusedMergeParts; ++p) {
+      bad |= oml[p].x != oml[p].x;
+      M = fmaxf(M, oml[p].x);
+    }
+    const float f0 = rM[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(rM[k] - M);
+    float num = f0 * rnum[k], den = f0 * rden[k];
+#pragma unroll
+    for (int p = 0; p < kFusedMergeParts; ++p) {
+      const float f = oml[p].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(oml[p].x - M);
+      den = fmaf(f, oml[p].y, den);
+      num = fmaf(f, ox[p], num);
+    }
+    out[row * D + d] = static_cast<T>(bad ? __builtin_nanf("") : num / den);
+  }
+}
+
+// Three workgroups per CU (12 waves) keep enough K/V loads in flight; the
+// register budget is pinned so the item loop does not trade occupancy for
+// registers. fp32 storage with large head tiles needs more registers.
+template <typename T, int D, int GT> constexpr int decode_waves_per_eu() {
+  return (sizeof(T) == 2 || GT <= 4) ? 3 : 2;
+}
+
+template <typename T, int D, int GT>
+__global__ __launch_bounds__(kDecodeWaves * 64)
+__attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT>()))) void paged_decode_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[Cfg<T, D, GT>::kSmem];
+  // Work items. The hardware deals workgroup i to XCD i % 8, and workgroups
+  // start in index order as slots free up. The unit (KV head x query-head
+  // chunk) varies fastest, so the sequences a KV head serves stay on one XCD
+  // and its L2 (shared-prefix blocks are read together). For batches of up to
+  // kCompactSeqs sequences, the wgs_per_unit workgroups of a unit walk that
+  // unit's items in longest-first order (make_plan), in boustrophedon rounds:
+  // workgroup w takes items w, 2G - 1 - w, 2G + w, ... (G = wgs_per_unit), so
+  // a workgroup that drew a long item early draws a short one next, and no
+  // workgroup is launched for the partitions that short sequences do not have.
+  // Larger batches take one item per workgroup in a fixed order:
+  // partition-major, the sequence rotated by the partition so the partitions
+  // of a long sequence spread over the chip.
+  const int units = a.n_kv_heads * a.head_chunks;
+  const int64_t lin = blockIdx.x;
+  const int unit = (int)(lin % units);
+  const int w = (int)(lin / units);
+  const bool compact = a.num_seqs <= kCompactSeqs;
+  ItemPlan plan;
+  if (compact) make_plan(a, plan);
+  for (int round = 0;; ++round) {
+    int s, part;
+    if (compact) {
+      const int G = a.wgs_per_unit;
+      const int64_t j = (int64_t)round * G + ((round & 1) ? G - 1 - w : w);
+      if (j >= plan.items) break;
+      locate_item(plan, a.num_seqs, (int)j, s, part);
+    } else {
+      if (round > 0) break;
+      part = w / a.num_seqs;
+      s = (w % a.num_seqs + a.num_seqs - part % a.num_seqs) % a.num_seqs;
+    }
+    s = __builtin_amdgcn_readfirstlane(s);
+    part = __builtin_amdgcn_readfirstlane(part);
+    if (round > 0) __syncthreads();  // the previous item's merge has read every wave's LDS
+    // An opaque copy of the thread index: lane-derived addresses are then
+    // recomputed per item instead of being hoisted out of the item loop and
+    // held in registers through the tile loop.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    decode_item<T, D, GT>(a, smem, tid, unit, s, part);
   }
 }
 
@@ -676,14 +905,123 @@ __global__ __launch_bounds__(kReduceThreads) void paged_decode_reduce_kernel(Dec
   }
 }
 
+// The same merge when the table width allows at most kFewParts partitions:
+// one thread per output element (query head, dimension) of kMergeHeadsPerThread
+// heads, every partial of those elements loaded at once and then combined.
+// A workgroup of kMergeThreads covers kMergeThreads / D * kMergeHeadsPerThread
+// heads of one sequence; workgroups of unsplit sequences return after reading
+// the length.
+constexpr int kFewParts = 8;
+constexpr int kMergeThreads = 256;
+constexpr int kMergeHeadsPerThread = 4;
+
+template <int D> __host__ __device__ constexpr int merge_heads_per_wg() {
+  return kMergeThreads / D * kMergeHeadsPerThread;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kMergeThreads) void paged_decode_merge_few_kernel(DecodeArgs a) {
+  constexpr int kHL = kMergeThreads / D;  // head lanes per workgroup
+  constexpr int kHPT = kMergeHeadsPerThread;
+  constexpr int kHW = merge_heads_per_wg<D>();
+  const int hblocks = (a.n_heads + kHW - 1) / kHW;
+  const int s = blockIdx.x / hblocks;
+  const int hb = blockIdx.x - s * hblocks;
+  const int L = a.seq_lens[s];
+  const int P = a.partition_tokens;
+  if (L <= P || (int64_t)L > (int64_t)a.max_blocks * a.block_size) return;  // single partition or invalid
+  const int nparts = (L + P - 1) / P;  // 2 .. max_parts <= kFewParts
+  const int d = threadIdx.x % D;
+  const int hl = threadIdx.x / D;
+  float2 ml[kHPT][kFewParts];
+  float x[kHPT][kFewParts];
+#pragma unroll
+  for (int j = 0; j < kHPT; ++j) {
+    const int h = hb * kHW + j * kHL + hl;
+    const int64_t row = ((int64_t)s * a.n_heads + h) * a.max_parts;
+#pragma unroll
+    for (int p = 0; p < kFewParts; ++p) {
+      if (h < a.n_heads && p < nparts) {
+        ml[j][p] = a.part_ml[row + p];
+        x[j][p] = a.part_acc[(row + p) * D + d];
+      } else {
+        ml[j][p] = make_float2(-INFINITY, 0.f);
+        x[j][p] = 0.f;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kHPT; ++j) {
+    const int h = hb * kHW + j * kHL + hl;
+    if (h >= a.n_heads) continue;
+    float M = -INFINITY;
+    bool bad = false;
+#pragma unroll
+    for (int p = 0; p < kFewParts; ++p) {
+      bad |= ml[j][p].x != ml[j][p].x;
+      M = fmaxf(M, ml[j][p].x);
+    }
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int p = 0; p < kFewParts; ++p) {
+      const float f = ml[j][p].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[j][p].x - M);
+      den = fmaf(f, ml[j][p].y, den);
+      num = fmaf(f, x[j][p], num);
+    }
+    static_cast<T *>(a.out)[((int64_t)s * a.n_heads + h) * D + d] =
+        static_cast<T>(bad ? __builtin_nanf("") : num / den);
+  }
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Decode workgroups per unit in the longest-first mode: at least one per
+// sequence and enough for kWgsPerSlot rounds of the chip's resident slots,
+// never more than the unit's largest possible item count.
+constexpr int kWgsPerSlot = 2;
+
 template <typename T, int D, int GT>
-hipError_t launch_t(const DecodeArgs &a, hipStream_t stream) {
-  dim3 grid((unsigned)((int64_t)a.n_kv_heads * a.head_chunks * a.num_seqs * a.max_parts), 1, 1);
+hipError_t launch_t(const DecodeArgs &args, hipStream_t stream) {
+  DecodeArgs a = args;
+  const int64_t units = (int64_t)a.n_kv_heads * a.head_chunks;
+  const int64_t max_items = (int64_t)a.num_seqs * a.max_parts;
+  if (a.num_seqs <= kCompactSeqs) {
+    static const int per_cu = [] {
+      int nb = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, paged_decode_kernel<T, D, GT>, kDecodeWaves * 64, 0) !=
+              hipSuccess || nb <= 0)
+        nb = 1;
+      return nb;
+    }();
+    const int64_t slots = (int64_t)per_cu * device_cus() * kWgsPerSlot;
+    int64_t g = (slots + units - 1) / units;
+    if (g < a.num_seqs) g = a.num_seqs;
+    a.wgs_per_unit = (int32_t)(g < max_items ? g : max_items);
+  } else {
+    a.wgs_per_unit = (int32_t)max_items;
+  }
+  dim3 grid((unsigned)(units * a.wgs_per_unit), 1, 1);
   hipLaunchKernelGGL((paged_decode_kernel<T, D, GT>), grid, dim3(kDecodeWaves * 64), 0, stream, a);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || a.max_parts == 1) return err;
-  dim3 rgrid(a.n_heads, a.num_seqs, 1);
-  hipLaunchKernelGGL((paged_decode_reduce_kernel<T, D>), rgrid, dim3(kReduceThreads), 0, stream, a);
+  if (err != hipSuccess || a.max_parts == 1 || a.arrivals != nullptr) return err;
+  if (a.max_parts <= kFewParts) {
+    const int hblocks = (a.n_heads + merge_heads_per_wg<D>() - 1) / merge_heads_per_wg<D>();
+    hipLaunchKernelGGL((paged_decode_merge_few_kernel<T, D>), dim3((unsigned)(a.num_seqs * hblocks)),
+                       dim3(kMergeThreads), 0, stream, a);
+  } else {
+    dim3 rgrid(a.n_heads, a.num_seqs, 1);
+    hipLaunchKernelGGL((paged_decode_reduce_kernel<T, D>), rgrid, dim3(kReduceThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -708,7 +1046,20 @@ hipError_t launch_dt(int head_dim, int gt, const DecodeArgs &a, hipStream_t stre
   }
 }
 
+__global__ void zero_i32_kernel(int32_t *p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_zero_i32(int32_t *p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(zero_i32_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0,
+                     stream, p, n);
+  return hipGetLastError();
+}
 
 int decode_head_tile(int group) {
   int gt = 1;

@@ -37,14 +37,26 @@ struct DecodeArgs {
   int64_t num_blocks;
   int32_t partition_tokens;
   int32_t max_parts;
+  int32_t wgs_per_unit;    // decode workgroups per unit (set by launch_decode)
   float *part_acc;         // [num_seqs * n_heads * max_parts, head_dim] (only when max_parts > 1)
   float2 *part_ml;         // [num_seqs * n_heads * max_parts] (max in base-2 units, sum)
+  // Arrival counters [num_seqs * n_kv_heads * head_chunks], zero between calls;
+  // set when the partitions of a sequence are merged by the last of them to
+  // finish (max_parts <= kFusedMergeParts), null when a merge kernel runs.
+  int32_t *arrivals;
 };
+
+// Largest partition count merged inside the decode kernel; longer tables use
+// a separate merge kernel.
+constexpr int kFusedMergeParts = 8;
 
 // Head tile: query heads of one KV head processed by one workgroup (1, 2, 4, 8 or 16).
 int decode_head_tile(int group);
 
 hipError_t launch_decode(DType dt, int head_dim, const DecodeArgs &a, hipStream_t stream);
+
+// Sets n int32 words to zero with a kernel (no memset node, so it may be captured).
+hipError_t launch_zero_i32(int32_t *p, int64_t n, hipStream_t stream);
 
 struct CacheWriteArgs {
   void *k_pool;

@@ -190,6 +190,44 @@ def test_random_shapes(i, H, Hkv, D, BS, dtype):
     assert err <= TOL[dtype], (i, err)
 
 
+@pytest.mark.parametrize("num_seqs", [1, 63, 64, 65, 200, 256, 257])
+def test_batch_sizes_and_repeated_calls(num_seqs):
+    """Batch sizes around the 64-sequence chunks of the longest-first item order
+    and its 256-sequence limit; 32 KV heads so a workgroup takes several items.
+    Two calls in a row must agree with the oracle (the in-kernel merge leaves its
+    arrival counters at zero)."""
+    say(f"batch of {num_seqs}")
+    w = workloads.random_case(4000 + num_seqs, num_seqs=num_seqs, n_heads=32, n_kv_heads=32,
+                              head_dim=64, block_size=16, dtype=torch.bfloat16, max_len=2600,
+                              poison=True)
+    g = OnGpu(w)
+    ref = oracle_decode(w, w.seq_lens, w.k_pool, w.v_pool)
+    for call in range(2):
+        out = g.decode()
+        torch.cuda.synchronize()
+        err = max_abs_err(out, ref)
+        say(f"  call {call}: max abs err {err:.3e}")
+        assert err <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("partition", [192, 176])
+def test_merge_at_partition_count_limit(partition):
+    """8 partitions per sequence are merged inside the decode kernel, 9 by the
+    separate merge kernel."""
+    _lib.set_partition_tokens(partition)
+    w = workloads.random_case(31 + partition, num_seqs=5, n_heads=8, n_kv_heads=2, head_dim=128,
+                              block_size=16, dtype=torch.float16, max_len=1500, min_len=1300,
+                              poison=True)
+    nparts = _lib.decode_plan(w.n_heads, w.n_kv_heads, w.block_size, w.num_seqs,
+                              w.max_blocks_per_seq)[1]
+    assert nparts == (8 if partition == 192 else 9)
+    g = OnGpu(w)
+    ref = oracle_decode(w, w.seq_lens, w.k_pool, w.v_pool)
+    for _ in range(2):
+        out = g.decode()
+        assert max_abs_err(out, ref) <= TOL[w.dtype]
+
+
 def test_many_short_sequences():
     w = workloads.random_case(77, num_seqs=1500, n_heads=8, n_kv_heads=8, head_dim=64,
                               block_size=16, dtype=torch.float16, max_len=40)
