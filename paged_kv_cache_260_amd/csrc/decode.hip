@@ -186,7 +186,11 @@ template <typename T, int D, int GT> struct Cfg {
   static constexpr int kMlOff = kNW * kWaveBytes;        // workgroup-wide
   static constexpr int kBadOff = kMlOff + kNW * GT * 8;
   static constexpr int kFlagOff = kBadOff + kNW * 4;
-  static constexpr int kSmem = kFlagOff + 4;
+  // Q of the item (its GT head rows, swizzled like a K tile), shared by the
+  // four waves as the MFMA A operand; rows GT..15 of the operand are zero
+  static constexpr int kQOff = (kFlagOff + 4 + 15) / 16 * 16;
+  static constexpr int kQChunks = GT * kCh;
+  static constexpr int kSmem = kQOff + kQChunks * 16;
   static_assert(kCh % 4 == 0 && 64 % kCh == 0, "head_dim must give 8, 16 or 32 chunks");
   static_assert(!kPvMfma || kCh == 8 || kCh == 16, "MFMA P*V path: 8 or 16 chunks per row");
   static_assert(GT >= 1 && GT <= 16, "head tile");
@@ -240,13 +244,17 @@ __device__ __forceinline__ void make_plan(const DecodeArgs &a, ItemPlan &pl) {
   const int B = a.num_seqs;
   const int P = a.partition_tokens;
   const int64_t max_tok = (int64_t)a.max_blocks * a.block_size;
+  // all chunk loads first (clamped index, no branches), so they are in flight
+  // together and one wait covers them
+  int Ls[kCompactChunks];
+#pragma unroll
+  for (int c = 0; c < kCompactChunks; ++c) Ls[c] = a.seq_lens[min(c * 64 + lane, B - 1)];
   int full_sum = 0;
 #pragma unroll
   for (int c = 0; c < kCompactChunks; ++c) {
     pl.fb[c] = 15;
-    const int sq = c * 64 + lane;
-    if (sq < B) {
-      const int L = a.seq_lens[sq];
+    if (c * 64 + lane < B) {
+      const int L = Ls[c];
       const bool ok = L > 0 && (int64_t)L <= max_tok;
       const int full = ok ? (L - 1) / P : 0;
       const int rem = L - full * P;  // 1 .. P when ok
@@ -337,12 +345,19 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   const int32_t *bt_row = a.block_tables + (int64_t)s * a.max_blocks;
   const int jb = start >> a.block_shift;
   const int btv_raw = jb + lane < a.max_blocks ? bt_row[jb + lane] : 0;
-  u32x4_t qa[C::kSteps];
+  // Q chunks of this thread: chunk u = tid + 256 i of the GT x kCh head-row
+  // block (rows past nh are zero)
+  constexpr int kQPer = (C::kQChunks + kNW * 64 - 1) / (kNW * 64);
+  u32x4_t qv[kQPer];
   {
-    const u32x4_t *qrow = reinterpret_cast<const u32x4_t *>(
-        static_cast<const T *>(a.q) + ((int64_t)s * H + head0 + min(n, nh - 1)) * D);
+    const u32x4_t *qblk = reinterpret_cast<const u32x4_t *>(static_cast<const T *>(a.q) +
+                                                            ((int64_t)s * H + head0) * D);
 #pragma unroll
-    for (int c = 0; c < C::kSteps; ++c) qa[c] = qrow[kg + 4 * c];
+    for (int i = 0; i < kQPer; ++i) {
+      const int u = tid + i * kNW * 64;
+      qv[i] = u32x4_t{0u, 0u, 0u, 0u};
+      if (u < C::kQChunks && u / kCh < nh) qv[i] = qblk[u];
+    }
   }
   const int L = a.seq_lens[s];
   const bool bad_len = L < 0 || (int64_t)L > (int64_t)a.max_blocks * a.block_size;
@@ -357,12 +372,6 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   if (start >= L) return;
   const int end = min(L, start + P);
   const int nparts = (L + P - 1) / P;
-
-  // Q as the MFMA A operand: row n = query head (zero past nh), k = head dims
-  if (n >= nh) {
-#pragma unroll
-    for (int c = 0; c < C::kSteps; ++c) qa[c] = u32x4_t{0u, 0u, 0u, 0u};
-  }
 
   // Block ids of the partition (at most 64 table entries): lane i of btv holds
   // entry jb + i. They are read back with v_readlane, so the per-tile lookup
@@ -406,6 +415,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   u32x4_t *kst = reinterpret_cast<u32x4_t *>(wreg + C::kKstOff);
   char *vst = wreg + C::kVstOff;
   char *pst = wreg + C::kPstOff;
+  const u32x4_t *qs = reinterpret_cast<const u32x4_t *>(smem + C::kQOff);
 
   // Running softmax state per head row: lanes (kg, n) own heads 4 kg + r.
   // m[r] is a reference max in base-2 units, uniform across the 16 lanes of
@@ -488,7 +498,9 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
     }
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < C::kSteps; ++c) sc = mfma_chunk<T>(qa[c], kst[kst_slot<kCh>(n, kg + 4 * c)], sc);
+    for (int c = 0; c < C::kSteps; ++c)
+      sc = mfma_chunk<T>(n < GT ? qs[kst_slot<kCh>(n, kg + 4 * c)] : u32x4_t{0u, 0u, 0u, 0u},
+                         kst[kst_slot<kCh>(n, kg + 4 * c)], sc);
 
     // scores in base-2 units; tokens past the sequence get -inf
     const bool tok_ok = n < valid;
@@ -591,14 +603,22 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   // load, then use.
   const int tb = start / kTileTokens;
   const int te = (end + kTileTokens - 1) / kTileTokens;
+  Regs rg;
   if constexpr (C::kPvMfma) {
-    Regs rg;
-    int ti = tb + wave;
-    if (ti < te) load_tile(ti, rg);
-    for (; ti < te; ti += kNW) process(ti, rg, ti + kNW < te ? ti + kNW : -1);
+    if (tb + wave < te) load_tile(tb + wave, rg);
+  }
+  // the item's Q, shared by the waves, goes to LDS while those loads fly
+#pragma unroll
+  for (int i = 0; i < kQPer; ++i) {
+    const int u = tid + i * kNW * 64;
+    if (u < C::kQChunks)
+      reinterpret_cast<u32x4_t *>(smem + C::kQOff)[kst_slot<kCh>(u / kCh, u % kCh)] = qv[i];
+  }
+  __syncthreads();
+  if constexpr (C::kPvMfma) {
+    for (int ti = tb + wave; ti < te; ti += kNW) process(ti, rg, ti + kNW < te ? ti + kNW : -1);
   } else {
     for (int ti = tb + wave; ti < te; ti += kNW) {
-      Regs rg;
       load_tile(ti, rg);
       process(ti, rg, -1);
     }
