@@ -34,7 +34,11 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 DECODE_SRC = os.path.join(PKG, "csrc", "decode.hip")
 DECODE_KERNEL = "paged_decode_kernel"
 MERGE_KERNEL = "paged_decode_reduce_kernel"
+MERGE_FEW_KERNEL = "paged_decode_merge_few_kernel"
 COPY_KERNEL = "copyBuffer"
+# kernels of one paged_attn_decode call (the merge kernels run only for split
+# sequences whose partitions are not merged inside the decode kernel)
+CALL_KERNELS = (DECODE_KERNEL, MERGE_KERNEL, MERGE_FEW_KERNEL)
 
 
 def source_hash(path: str = DECODE_SRC) -> str:
@@ -43,7 +47,7 @@ def source_hash(path: str = DECODE_SRC) -> str:
 
 
 def short_name(name: str) -> str:
-    for key in (DECODE_KERNEL, MERGE_KERNEL, "kv_cache_write_kernel", COPY_KERNEL):
+    for key in (*CALL_KERNELS, "kv_cache_write_kernel", "zero_i32_kernel", COPY_KERNEL):
         if key in name:
             return key
     return name[:60]
@@ -99,7 +103,9 @@ def summarize(name, command, stats_csv, fetch_csv, write_csv, algorithmic_bytes,
             return sum(v) / len(v) if v else 0.0
 
         per_kernel = {}
-        for k in (DECODE_KERNEL, MERGE_KERNEL):
+        for k in CALL_KERNELS:
+            if not fetch.get(k):
+                continue
             per_kernel[k] = {"fetch_kib_raw": avg(fetch, k), "write_kib_raw": avg(write, k),
                              "fetch_bytes": avg(fetch, k) * f_scale * 1024,
                              "write_bytes": avg(write, k) * w_scale * 1024}
