@@ -115,6 +115,50 @@ def cpu_baseline(w, lens_after, kp_after, vp_after, budget_s):
                       f"numpy fp64, one Python thread driving BLAS with {threads} threads"}
 
 
+def bench_copy_blocks(args, dev):
+    """Copy-on-write block copy: pairs of 32 KiB bf16 blocks (8 KV heads x 16
+    tokens x 128 dims) in both pools, timed with HIP events on the stream.
+    Two workloads: one copy per sequence of a 128-sequence batch (what a
+    parallel-sampling step asks for) and 8192 pairs (bandwidth)."""
+    Hkv, BS, D, dt = 8, 16, 128, torch.bfloat16
+    block_bytes = Hkv * BS * D * 2
+    results = {}
+    for name, npairs in (("cow_step_b128", 128), ("bulk_8192", 8192)):
+        nb = 4 * npairs + 64
+        reps = max(3, math.ceil(3 * MALL_BYTES / (2 * nb * block_bytes)))
+        pools = [(torch.randn(nb, Hkv, BS, D, device=dev).to(dt), torch.randn(nb, Hkv, BS, D, device=dev).to(dt))
+                 for _ in range(reps)]
+        rng = np.random.default_rng(npairs)
+        perm = rng.permutation(nb)
+        pairs = torch.from_numpy(np.stack([perm[npairs:2 * npairs], perm[:npairs]], 1).astype(np.int32)).to(dev)
+        for i in range(args.warmup):
+            _lib.copy_blocks(*pools[i % reps], pairs)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.steps):
+            _lib.copy_blocks(*pools[i % reps], pairs)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        moved = 2 * 2 * npairs * block_bytes  # K and V, read + write
+        results[name] = {"pairs": npairs, "us": round(us, 3), "bytes": moved,
+                         "GBps": round(moved / (us * 1e-6) / 1e9, 1)}
+        del pools
+        torch.cuda.empty_cache()
+    bulk = results["bulk_8192"]
+    print(json.dumps({
+        "metric": "copy_blocks HBM GB/s (read + write, both pools)", "value": bulk["GBps"], "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "copy-on-write block copy, 32 KiB blocks (Hkv 8, BS 16, D 128, bf16)",
+                   **{k: v for k, v in results.items()}},
+        "roofline": {"bound": "hbm", "achieved": bulk["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(bulk["GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "copy_blocks_kernel", "algorithmic_bytes": bulk["bytes"]},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,6 +171,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks"],
+                    help="decode = the hot-path step (default); copy_blocks = copy-on-write block copy")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -139,6 +185,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     _lib.lib()
+    if args.op == "copy_blocks":
+        bench_copy_blocks(args, dev)
+        return
     _lib.set_partition_tokens(args.partition)
 
     log(f"[bench] building workload config {args.config}")

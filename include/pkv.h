@@ -55,7 +55,8 @@ typedef enum {
   PKV_OK = 0,
   PKV_ERR_INVALID = 1,      /* bad argument: null pointer, shape, alignment, size */
   PKV_ERR_UNSUPPORTED = 2,  /* valid but not built: head_dim, block_size or dtype */
-  PKV_ERR_DEVICE = 3        /* a HIP call failed (launch, allocation, device query) */
+  PKV_ERR_DEVICE = 3,       /* a HIP call failed (launch, allocation, device query) */
+  PKV_ERR_NO_BLOCKS = 4     /* the block manager's free queue is too short (pkv_blocks.h) */
 } pkv_status;
 
 typedef enum {
@@ -101,9 +102,11 @@ typedef enum {
  *
  * Long sequences are split into partitions whose partial results (fp32) go to
  * a workspace owned by the library (grown on demand per device and stream,
- * released by pkv_release_workspace) and are merged by a second kernel on the
- * same stream. Two calls that run at the same time on one stream pair are not
- * supported; different streams get different workspaces.
+ * released by pkv_release_workspace). Up to 8 partitions per sequence are
+ * merged by the last of them to finish, inside the decode kernel; longer
+ * tables use a second kernel on the same stream. Two calls that run at the
+ * same time on one stream are not supported; different streams get
+ * different workspaces.
  */
 PKV_API int pkv_paged_attn_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
                           const int32_t *block_tables, const int32_t *seq_lens, float scale,

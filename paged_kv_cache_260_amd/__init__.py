@@ -3,12 +3,16 @@ slot-mapped cache write, as hand-written HIP kernels behind a C ABI
 (``include/pkv.h``).
 
 ``paged_attn_decode`` and ``kv_cache_write`` take torch tensors on the GPU and
-call the HIP library; the library is loaded on first use and a missing build
+call the HIP library; ``BlockManager`` (host) hands out pool blocks with
+reference-counted sharing and copy-on-write, whose copies ``copy_blocks`` runs
+on the GPU; the library is loaded on first use and a missing build
 raises. ``workloads`` builds seeded synthetic inputs; ``accounting`` holds the
 byte counts used to turn kernel time into bandwidth.
 """
 from ._lib import (  # noqa: F401
+    BlockManager,
     PkvError,
+    copy_blocks,
     decode_plan,
     kv_cache_write,
     last_error,
@@ -20,6 +24,8 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "paged_attn_decode",
+    "BlockManager",
+    "copy_blocks",
     "kv_cache_write",
     "decode_plan",
     "set_partition_tokens",

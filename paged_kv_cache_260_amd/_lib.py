@@ -1,4 +1,4 @@
-"""ctypes binding of ``libpkv.so`` (``include/pkv.h``).
+"""ctypes binding of ``libpkv.so`` (``include/pkv.h``, ``include/pkv_blocks.h``).
 
 Argument marshalling only: shapes, dtypes and devices of torch tensors are
 checked and turned into the raw pointers and sizes of the C ABI, together
@@ -17,7 +17,7 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
-PKV_OK, PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_DEVICE = 0, 1, 2, 3
+PKV_OK, PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_DEVICE, PKV_ERR_NO_BLOCKS = 0, 1, 2, 3, 4
 DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 _lock = threading.Lock()
@@ -35,6 +35,19 @@ _SIGNATURES = {
                                        ctypes.POINTER(_i32)]),
     "pkv_release_workspace": (ctypes.c_int, []),
     "pkv_version": (_i32, []),
+    # block manager and block copy (pkv_blocks.h)
+    "pkv_bm_create": (ctypes.c_int, [_i64, _i32, ctypes.POINTER(_vp)]),
+    "pkv_bm_destroy": (ctypes.c_int, [_vp]),
+    "pkv_bm_add_sequence": (ctypes.c_int, [_vp, _i64, _i32]),
+    "pkv_bm_fork": (ctypes.c_int, [_vp, _i64, _i64]),
+    "pkv_bm_append_slots": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, ctypes.POINTER(_i32)]),
+    "pkv_bm_free_sequence": (ctypes.c_int, [_vp, _i64]),
+    "pkv_bm_num_free": (ctypes.c_int, [_vp, ctypes.POINTER(_i64)]),
+    "pkv_bm_refcount": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_i32)]),
+    "pkv_bm_sequence": (ctypes.c_int, [_vp, _i64, ctypes.POINTER(_i32), ctypes.POINTER(_i32), _vp, _i32]),
+    "pkv_bm_build_tables": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp]),
+    "pkv_bm_free_queue": (ctypes.c_int, [_vp, _vp, _i64]),
+    "pkv_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
 }
 
 
@@ -164,3 +177,112 @@ def release_workspace() -> None:
 
 def version() -> int:
     return int(lib().pkv_version())
+
+
+def copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, pairs: torch.Tensor, stream=None) -> None:
+    """Copy whole pool blocks: ``pool[pairs[i, 1]] = pool[pairs[i, 0]]`` in both pools.
+
+    ``pairs`` is int32 ``[N, 2]`` (src, dst) on the pools' device; destinations
+    are distinct and are not sources (copy-on-write targets are fresh blocks).
+    """
+    dt = k_pool.dtype
+    _need(dt in DTYPE_CODES, f"unsupported dtype {dt}")
+    _dev_tensor(k_pool, "k_pool", dt)
+    _dev_tensor(v_pool, "v_pool", dt)
+    _dev_tensor(pairs, "pairs", torch.int32)
+    _need(k_pool.dim() == 4 and v_pool.shape == k_pool.shape, "pools must be [NB, Hkv, BS, D]")
+    _need(pairs.dim() == 2 and pairs.shape[1] == 2, "pairs must be [N, 2]")
+    _need(len({k_pool.device, v_pool.device, pairs.device}) == 1, "all tensors must be on one device")
+    NB, Hkv, BS, D = k_pool.shape
+    with torch.cuda.device(k_pool.device):
+        _check(lib().pkv_copy_blocks(k_pool.data_ptr(), v_pool.data_ptr(), pairs.data_ptr(),
+                                     pairs.shape[0], Hkv, D, BS, NB, DTYPE_CODES[dt],
+                                     _stream_handle(k_pool, stream)))
+
+
+class BlockManager:
+    """Host block manager of a pool of ``num_blocks`` blocks (``pkv_blocks.h``).
+
+    A FIFO free queue, a reference count per block, and per sequence its block
+    list and token count: blocks are allocated on demand, shared by forks,
+    copied on write and released last block first.
+    """
+
+    def __init__(self, num_blocks: int, block_size: int):
+        h = _vp()
+        _check(lib().pkv_bm_create(int(num_blocks), int(block_size), ctypes.byref(h)))
+        self._h = h
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) and self._h.value:
+            lib().pkv_bm_destroy(self._h)
+            self._h = _vp()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # pragma: no cover - interpreter shutdown
+            pass
+
+    def add_sequence(self, seq_id: int, num_tokens: int) -> None:
+        _check(lib().pkv_bm_add_sequence(self._h, int(seq_id), int(num_tokens)))
+
+    def fork(self, parent: int, child: int) -> None:
+        _check(lib().pkv_bm_fork(self._h, int(parent), int(child)))
+
+    def append_slots(self, seq_ids):
+        """Reserve the next token's slot of each sequence: ``(slots, copies)``,
+        numpy int32 ``[n]`` and ``[num_copies, 2]`` (src, dst)."""
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = ids.shape[0]
+        slots = np.empty(n, dtype=np.int32)
+        copies = np.empty((max(n, 1), 2), dtype=np.int32)
+        nc = _i32()
+        _check(lib().pkv_bm_append_slots(self._h, ids.ctypes.data, n, slots.ctypes.data,
+                                         copies.ctypes.data, ctypes.byref(nc)))
+        return slots, copies[:nc.value].copy()
+
+    def free_sequence(self, seq_id: int) -> None:
+        _check(lib().pkv_bm_free_sequence(self._h, int(seq_id)))
+
+    def num_free(self) -> int:
+        n = _i64()
+        _check(lib().pkv_bm_num_free(self._h, ctypes.byref(n)))
+        return n.value
+
+    def refcount(self, block: int) -> int:
+        c = _i32()
+        _check(lib().pkv_bm_refcount(self._h, int(block), ctypes.byref(c)))
+        return c.value
+
+    def sequence(self, seq_id: int):
+        """``(num_tokens, [block ids])`` of one sequence."""
+        import numpy as np
+        nt, nb = _i32(), _i32()
+        _check(lib().pkv_bm_sequence(self._h, int(seq_id), ctypes.byref(nt), ctypes.byref(nb), None, 0))
+        blocks = np.empty(max(nb.value, 1), dtype=np.int32)
+        _check(lib().pkv_bm_sequence(self._h, int(seq_id), ctypes.byref(nt), ctypes.byref(nb),
+                                     blocks.ctypes.data, nb.value))
+        return nt.value, [int(b) for b in blocks[:nb.value]]
+
+    def build_tables(self, seq_ids, max_blocks: int):
+        """Host ``(block_tables [n, max_blocks], seq_lens [n])`` (int32 numpy) for decode."""
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = ids.shape[0]
+        tables = np.empty((n, max_blocks), dtype=np.int32)
+        lens = np.empty(n, dtype=np.int32)
+        _check(lib().pkv_bm_build_tables(self._h, ids.ctypes.data, n, int(max_blocks),
+                                         tables.ctypes.data, lens.ctypes.data))
+        return tables, lens
+
+    def free_queue(self):
+        """Block ids of the free queue, front first."""
+        import numpy as np
+        n = self.num_free()
+        out = np.empty(max(n, 1), dtype=np.int32)
+        _check(lib().pkv_bm_free_queue(self._h, out.ctypes.data, n))
+        return [int(b) for b in out[:n]]

@@ -1,8 +1,8 @@
 """Build ``libpkv.so`` (the HIP library behind ``include/pkv.h``) for gfx950.
 
-Usage: ``python -m paged_kv_cache_260_amd.build``. Each ``csrc/*.hip`` file is
-compiled to an object in parallel with hipcc, then linked into one shared
-library next to this file. Packed-fp32 VALU instructions are disabled for
+Usage: ``python -m paged_kv_cache_260_amd.build``. Each ``csrc/*.hip`` (device
+and host) and ``csrc/*.cpp`` (host only) file is compiled to an object in
+parallel with hipcc, then linked into one shared library next to this file. Packed-fp32 VALU instructions are disabled for
 every HIP translation unit (see the ``-packed-fp32-ops`` flag).
 """
 from __future__ import annotations
@@ -52,7 +52,7 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     """Compile every HIP source and link ``libpkv.so``; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
-    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     if not sources:
         raise RuntimeError(f"no HIP sources under {CSRC}")
     with cf.ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:

@@ -4,6 +4,7 @@
 // before the first HIP call, so a bad call returns a status without touching
 // the device (and can be exercised on a machine with no GPU).
 #include "pkv.h"
+#include "pkv_blocks.h"
 
 #include <atomic>
 #include <cmath>
@@ -15,12 +16,13 @@
 #include <utility>
 
 #include "kernels.h"
+#include "status.h"
 
-namespace {
+namespace pkv {
 
 thread_local std::string g_error;
 
-int fail(int status, const char *fmt, ...) {
+int set_error(int status, const char *fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -30,10 +32,20 @@ int fail(int status, const char *fmt, ...) {
   return status;
 }
 
-int ok() {
+int clear_error() {
   g_error.clear();
   return PKV_OK;
 }
+
+}  // namespace pkv
+
+namespace {
+
+template <typename... Args> int fail(int status, const char *fmt, Args... args) {
+  return pkv::set_error(status, fmt, args...);
+}
+
+int ok() { return pkv::clear_error(); }
 
 int hip_fail(hipError_t e, const char *what) {
   return fail(PKV_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
@@ -143,7 +155,7 @@ int get_arrivals(hipStream_t stream, int64_t count, int32_t **out) {
 
 extern "C" {
 
-const char *pkv_last_error(void) { return g_error.c_str(); }
+const char *pkv_last_error(void) { return pkv::g_error.c_str(); }
 
 int32_t pkv_version(void) { return (1 << 16) | 0; }
 
@@ -275,6 +287,34 @@ int pkv_kv_cache_write(void *k_pool, void *v_pool, const void *k_new, const void
   a.num_slots = num_blocks * block_size;
   hipError_t e = pkv::launch_cache_write(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "cache write launch");
+  return ok();
+}
+
+int pkv_copy_blocks(void *k_pool, void *v_pool, const int32_t *pairs, int32_t num_pairs,
+                    int32_t n_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                    int32_t dtype, void *stream) {
+  if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID, "unknown dtype %d", dtype);
+  if (num_pairs < 0) return fail(PKV_ERR_INVALID, "num_pairs %d < 0", num_pairs);
+  if (n_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1)
+    return fail(PKV_ERR_INVALID, "n_kv_heads, head_dim, block_size and num_blocks must be >= 1");
+  const int64_t block_bytes = (int64_t)n_kv_heads * block_size * head_dim *
+                              pkv::dtype_bytes(static_cast<pkv::DType>(dtype));
+  if (block_bytes % 16 != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "block of %lld bytes is not a multiple of 16", (long long)block_bytes);
+  if (num_pairs == 0) return ok();
+  if (!k_pool || !v_pool || !pairs) return fail(PKV_ERR_INVALID, "null pointer");
+  if (!aligned16(k_pool) || !aligned16(v_pool)) return fail(PKV_ERR_INVALID, "pools must be 16-byte aligned");
+  if (block_bytes / 16 > (int64_t)65535 * 2048)
+    return fail(PKV_ERR_UNSUPPORTED, "block of %lld bytes is too large", (long long)block_bytes);
+  pkv::CopyBlocksArgs a{};
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.pairs = pairs;
+  a.num_pairs = num_pairs;
+  a.block_units = block_bytes / 16;
+  a.num_blocks = num_blocks;
+  hipError_t e = pkv::launch_copy_blocks(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "copy_blocks launch");
   return ok();
 }
 

@@ -73,4 +73,15 @@ struct CacheWriteArgs {
 
 hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t stream);
 
+struct CopyBlocksArgs {
+  void *k_pool;
+  void *v_pool;
+  const int32_t *pairs;    // [num_pairs, 2] (src, dst)
+  int32_t num_pairs;
+  int64_t block_units;     // 16-byte units per block of one pool
+  int64_t num_blocks;
+};
+
+hipError_t launch_copy_blocks(const CopyBlocksArgs &a, hipStream_t stream);
+
 }  // namespace pkv
