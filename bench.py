@@ -86,8 +86,10 @@ def stream_ceiling(device, nbytes=2 * 2 ** 30, iters=10):
     return read, copy
 
 
-def cpu_baseline(w, lens_after, kp_after, vp_after, budget_s):
-    """The fp64 oracle on the same batch on host cores, repeated for ~budget_s."""
+def cpu_baseline(w, lens_after, kp_after, vp_after, budget_s, fp8_scales=None):
+    """The fp64 oracle on the same batch on host cores, repeated for ~budget_s.
+    With ``fp8_scales`` = (k_scale, v_scale) the pools are e4m3 codes and the
+    oracle's FP8 decode (dequantize, then attend) runs instead."""
     import oracle  # test infrastructure: only this leg of the benchmark runs it
     try:
         from threadpoolctl import threadpool_info
@@ -95,19 +97,28 @@ def cpu_baseline(w, lens_after, kp_after, vp_after, budget_s):
     except Exception:  # pragma: no cover
         threads = 1
     qn = w.q.float().numpy()
-    kp = kp_after.float().numpy()
-    vp = vp_after.float().numpy()
+    if fp8_scales is None:
+        kp = kp_after.float().numpy()
+        vp = vp_after.float().numpy()
+    else:
+        kp, vp = kp_after.numpy(), vp_after.numpy()
+        ks, vs = (t.cpu().numpy() for t in fp8_scales)
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.paged_attn_decode(qn, kp, vp, w.block_tables, lens_after, w.scale, w.n_heads,
-                                 w.n_kv_heads, w.head_dim, w.block_size)
+        if fp8_scales is None:
+            oracle.paged_attn_decode(qn, kp, vp, w.block_tables, lens_after, w.scale, w.n_heads,
+                                     w.n_kv_heads, w.head_dim, w.block_size)
+        else:
+            oracle.fp8.paged_attn_decode_fp8(qn, kp, vp, ks, vs, w.block_tables, lens_after, w.scale,
+                                             w.n_heads, w.n_kv_heads, w.head_dim, w.block_size)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
     per = el / reps
-    nbytes = accounting.decode_compulsory_bytes(lens_after, w.n_heads, w.n_kv_heads, w.head_dim,
-                                                w.elem_bytes)
+    nbytes = (accounting.decode_kv_bytes(lens_after, w.n_kv_heads, w.head_dim,
+                                         1 if fp8_scales is not None else w.elem_bytes)
+              + accounting.decode_qo_bytes(w.num_seqs, w.n_heads, w.head_dim, w.elem_bytes))
     return {"value": round(nbytes / per / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"whole batch ({w.num_seqs} seqs, {int(np.sum(lens_after))} tokens), "
@@ -173,6 +184,8 @@ def main():
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks"],
                     help="decode = the hot-path step (default); copy_blocks = copy-on-write block copy")
+    ap.add_argument("--kv", default="native", choices=["native", "fp8"],
+                    help="KV pool storage: the query dtype (default) or FP8 e4m3 codes with per-head scales")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -195,7 +208,20 @@ def main():
     lens0 = w.seq_lens
     lens1 = w.seq_lens_after_write()
     e = w.elem_bytes
-    pool_bytes = 2 * w.k_pool.numel() * e
+    fp8 = args.kv == "fp8"
+    if fp8:
+        if w.dtype == torch.float32:
+            print("FP8 pools need a 16-bit workload", file=sys.stderr)
+            sys.exit(2)
+        # FP8 pools of the same workload: per-head scale amax / 448, codes by
+        # torch's e4m3 conversion (input generation only)
+        def to_codes(pool):
+            sc = pool.float().abs().amax(dim=(0, 2, 3)).clamp_min(1e-6) / 448.0
+            return (pool.float() / sc[None, :, None, None]).to(torch.float8_e4m3fn).view(torch.uint8), sc
+        k_codes, k_sc = to_codes(w.k_pool)
+        v_codes, v_sc = to_codes(w.v_pool)
+    e_kv = 1 if fp8 else e
+    pool_bytes = 2 * w.k_pool.numel() * e_kv
     R = args.replicas or max(3, math.ceil(3 * MALL_BYTES / pool_bytes))
     log(f"[bench] pools {pool_bytes / 2**20:.0f} MiB x {R} replicas")
     q = w.q.to(dev)
@@ -205,19 +231,28 @@ def main():
     slots = torch.from_numpy(w.slot_mapping).to(dev)
     kn = w.k_new.to(dev)
     vn = w.v_new.to(dev)
-    kps = [w.k_pool.to(dev)]
-    vps = [w.v_pool.to(dev)]
+    kps = [(k_codes if fp8 else w.k_pool).to(dev)]
+    vps = [(v_codes if fp8 else w.v_pool).to(dev)]
+    if fp8:
+        ksd, vsd = k_sc.to(dev), v_sc.to(dev)
     for _ in range(R - 1):
         kps.append(kps[0].clone())
         vps.append(vps[0].clone())
     stream = torch.cuda.current_stream(dev)
 
     def step(r, ev=None):
-        _lib.kv_cache_write(kps[r], vps[r], kn, vn, slots, stream=stream)
+        if fp8:
+            _lib.kv_cache_write_fp8(kps[r], vps[r], kn, vn, ksd, vsd, slots, stream=stream)
+        else:
+            _lib.kv_cache_write(kps[r], vps[r], kn, vn, slots, stream=stream)
         if ev is not None:
             ev[0].record(stream)
-        _lib.paged_attn_decode(out, q, kps[r], vps[r], bt, sl, w.scale, w.n_heads, w.n_kv_heads,
-                               w.head_dim, w.block_size, stream=stream)
+        if fp8:
+            _lib.paged_attn_decode_fp8(out, q, kps[r], vps[r], ksd, vsd, bt, sl, w.scale, w.n_heads,
+                                       w.n_kv_heads, w.head_dim, w.block_size, stream=stream)
+        else:
+            _lib.paged_attn_decode(out, q, kps[r], vps[r], bt, sl, w.scale, w.n_heads, w.n_kv_heads,
+                                   w.head_dim, w.block_size, stream=stream)
         if ev is not None:
             ev[1].record(stream)
 
@@ -243,8 +278,10 @@ def main():
     dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
     log(f"[bench] wall {wall * 1e3 / K:.4f} ms/step, events {ms_step:.4f} ms/step")
 
-    dec_bytes = accounting.decode_compulsory_bytes(lens1, w.n_heads, w.n_kv_heads, w.head_dim, e)
-    wr_bytes = accounting.write_bytes(int((w.slot_mapping >= 0).sum()), w.n_kv_heads, w.head_dim, e)
+    dec_bytes = (accounting.decode_kv_bytes(lens1, w.n_kv_heads, w.head_dim, e_kv)
+                 + accounting.decode_qo_bytes(w.num_seqs, w.n_heads, w.head_dim, e))
+    n_written = int((w.slot_mapping >= 0).sum())
+    wr_bytes = 2 * n_written * w.n_kv_heads * w.head_dim * (e + e_kv)  # read new rows, write pool rows
     step_bytes = dec_bytes + wr_bytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
     dec_mean = float(dec_ms.mean())
@@ -263,10 +300,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": DTYPE_NAMES[w.dtype],
+        "dtype": DTYPE_NAMES[w.dtype] + ("/fp8-e4m3 KV" if fp8 else ""),
         "data": "synthetic",
         "config": {
-            "workload": w.name,
+            "workload": w.name + (" with FP8 e4m3 KV pools (per-head scales)" if fp8 else ""),
             "batch": w.num_seqs, "n_heads": w.n_heads, "n_kv_heads": w.n_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size,
             "cached_tokens": int(lens1.sum()), "mean_seq_len": round(float(lens1.mean()), 1),
@@ -283,7 +320,7 @@ def main():
         "step_bytes": int(step_bytes),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(args.config),
+                     "traffic": None if fp8 else measured_traffic(args.config),
                      "kernel": "paged_attn_decode call (decode kernel"
                                + (")" if nparts == 1 else
                                   ", partitions merged in-kernel)" if nparts <= FUSED_MERGE_PARTS else
@@ -300,7 +337,8 @@ def main():
         torch.cuda.synchronize()
         kp_after = kps[0].cpu()
         vp_after = vps[0].cpu()
-        result["cpu_baseline"] = cpu_baseline(w, lens1, kp_after, vp_after, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, lens1, kp_after, vp_after, args.cpu_seconds,
+                                              (ksd, vsd) if fp8 else None)
     print(json.dumps(result), flush=True)
 
 

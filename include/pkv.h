@@ -62,7 +62,8 @@ typedef enum {
 typedef enum {
   PKV_F32 = 0,
   PKV_F16 = 1,
-  PKV_BF16 = 2
+  PKV_BF16 = 2,
+  PKV_FP8_E4M3 = 3  /* 1-byte OCP e4m3 pool codes (pkv_fp8.h); copy_blocks only here */
 } pkv_dtype;
 
 /*

@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for paged decode and the slot-mapped cache write.
+"""fp64 CPU oracle for paged decode, the slot-mapped cache write, the block
+manager and block copy, and the FP8 (e4m3) KV cache.
 
 TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import or run anything in this
@@ -17,3 +18,5 @@ from .paged_attention import (  # noqa: F401
     paged_attn_decode_partitioned,
 )
 from .cache_write import kv_cache_write  # noqa: F401
+from .block_manager import BlockManagerModel, copy_blocks  # noqa: F401
+from . import fp8  # noqa: F401

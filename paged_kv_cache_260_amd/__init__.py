@@ -15,8 +15,10 @@ from ._lib import (  # noqa: F401
     copy_blocks,
     decode_plan,
     kv_cache_write,
+    kv_cache_write_fp8,
     last_error,
     paged_attn_decode,
+    paged_attn_decode_fp8,
     release_workspace,
     set_partition_tokens,
     version,
@@ -26,6 +28,8 @@ __all__ = [
     "paged_attn_decode",
     "BlockManager",
     "copy_blocks",
+    "paged_attn_decode_fp8",
+    "kv_cache_write_fp8",
     "kv_cache_write",
     "decode_plan",
     "set_partition_tokens",

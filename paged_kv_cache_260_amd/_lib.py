@@ -1,4 +1,5 @@
-"""ctypes binding of ``libpkv.so`` (``include/pkv.h``, ``include/pkv_blocks.h``).
+"""ctypes binding of ``libpkv.so`` (``include/pkv.h``, ``include/pkv_blocks.h``,
+``include/pkv_fp8.h``).
 
 Argument marshalling only: shapes, dtypes and devices of torch tensors are
 checked and turned into the raw pointers and sizes of the C ABI, together
@@ -19,6 +20,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_DEVICE, PKV_ERR_NO_BLOCKS = 0, 1, 2, 3, 4
 DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+PKV_FP8_E4M3 = 3  # 1-byte pool codes (torch.uint8 tensors)
 
 _lock = threading.Lock()
 _lib: Optional[ctypes.CDLL] = None
@@ -48,6 +50,11 @@ _SIGNATURES = {
     "pkv_bm_build_tables": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp]),
     "pkv_bm_free_queue": (ctypes.c_int, [_vp, _vp, _i64]),
     "pkv_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
+    # FP8 (e4m3) KV cache (pkv_fp8.h)
+    "pkv_paged_attn_decode_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32,
+                                                 _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
+    "pkv_kv_cache_write_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                              _i64, _i32, _vp]),
 }
 
 
@@ -186,7 +193,7 @@ def copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, pairs: torch.Tensor,
     are distinct and are not sources (copy-on-write targets are fresh blocks).
     """
     dt = k_pool.dtype
-    _need(dt in DTYPE_CODES, f"unsupported dtype {dt}")
+    _need(dt in DTYPE_CODES or dt == torch.uint8, f"unsupported dtype {dt}")
     _dev_tensor(k_pool, "k_pool", dt)
     _dev_tensor(v_pool, "v_pool", dt)
     _dev_tensor(pairs, "pairs", torch.int32)
@@ -194,9 +201,10 @@ def copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, pairs: torch.Tensor,
     _need(pairs.dim() == 2 and pairs.shape[1] == 2, "pairs must be [N, 2]")
     _need(len({k_pool.device, v_pool.device, pairs.device}) == 1, "all tensors must be on one device")
     NB, Hkv, BS, D = k_pool.shape
+    code = PKV_FP8_E4M3 if dt == torch.uint8 else DTYPE_CODES[dt]
     with torch.cuda.device(k_pool.device):
         _check(lib().pkv_copy_blocks(k_pool.data_ptr(), v_pool.data_ptr(), pairs.data_ptr(),
-                                     pairs.shape[0], Hkv, D, BS, NB, DTYPE_CODES[dt],
+                                     pairs.shape[0], Hkv, D, BS, NB, code,
                                      _stream_handle(k_pool, stream)))
 
 
@@ -286,3 +294,66 @@ class BlockManager:
         out = np.empty(max(n, 1), dtype=np.int32)
         _check(lib().pkv_bm_free_queue(self._h, out.ctypes.data, n))
         return [int(b) for b in out[:n]]
+
+
+def paged_attn_decode_fp8(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
+                          v_pool: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor,
+                          block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                          n_heads: int, n_kv_heads: int, head_dim: int, block_size: int,
+                          stream=None) -> torch.Tensor:
+    """Decode over FP8 pools (uint8 e4m3 codes ``[NB, Hkv, BS, D]``, float32 scales ``[Hkv]``)."""
+    dt = q.dtype
+    _need(dt in (torch.float16, torch.bfloat16), f"FP8 pools need an fp16/bf16 query, got {dt}")
+    _dev_tensor(out, "out", dt)
+    _dev_tensor(q, "q", dt)
+    for name, t in (("k_pool", k_pool), ("v_pool", v_pool)):
+        _dev_tensor(t, name, torch.uint8)
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        _dev_tensor(t, name, torch.float32)
+        _need(t.shape == (n_kv_heads,), f"{name} must be [Hkv]")
+    _dev_tensor(block_tables, "block_tables", torch.int32)
+    _dev_tensor(seq_lens, "seq_lens", torch.int32)
+    B = q.shape[0]
+    _need(q.shape == (B, n_heads, head_dim) and out.shape == q.shape, "q/out must be [B, H, D]")
+    _need(k_pool.dim() == 4 and k_pool.shape[1:] == (n_kv_heads, block_size, head_dim),
+          "k_pool must be [NB, Hkv, BS, D]")
+    _need(v_pool.shape == k_pool.shape, "v_pool must match k_pool")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B, MB]")
+    _need(seq_lens.shape == (B,), "seq_lens must be [B]")
+    devs = {t.device for t in (out, q, k_pool, v_pool, k_scale, v_scale, block_tables, seq_lens)}
+    _need(len(devs) == 1, "all tensors must be on one device")
+    with torch.cuda.device(q.device):
+        _check(lib().pkv_paged_attn_decode_fp8(
+            out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_scale.data_ptr(),
+            v_scale.data_ptr(), block_tables.data_ptr(), seq_lens.data_ptr(), float(scale), n_heads,
+            n_kv_heads, head_dim, block_size, B, block_tables.shape[1], k_pool.shape[0],
+            DTYPE_CODES[dt], _stream_handle(q, stream)))
+    return out
+
+
+def kv_cache_write_fp8(k_pool: torch.Tensor, v_pool: torch.Tensor, k_new: torch.Tensor,
+                       v_new: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor,
+                       slot_mapping: torch.Tensor, stream=None) -> None:
+    """Quantize ``k_new``/``v_new`` (``[T, Hkv, D]``) into FP8 pools at ``slot_mapping``."""
+    dt = k_new.dtype
+    _need(dt in DTYPE_CODES, f"unsupported dtype {dt}")
+    for name, t in (("k_pool", k_pool), ("v_pool", v_pool)):
+        _dev_tensor(t, name, torch.uint8)
+    _dev_tensor(k_new, "k_new", dt)
+    _dev_tensor(v_new, "v_new", dt)
+    _dev_tensor(slot_mapping, "slot_mapping", torch.int32)
+    _need(k_pool.dim() == 4 and v_pool.shape == k_pool.shape, "pools must be [NB, Hkv, BS, D]")
+    NB, Hkv, BS, D = k_pool.shape
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        _dev_tensor(t, name, torch.float32)
+        _need(t.shape == (Hkv,), f"{name} must be [Hkv]")
+    T = k_new.shape[0]
+    _need(k_new.shape == (T, Hkv, D) and v_new.shape == k_new.shape, "k_new/v_new must be [T, Hkv, D]")
+    _need(slot_mapping.shape == (T,), "slot_mapping must be [T]")
+    devs = {t.device for t in (k_pool, v_pool, k_new, v_new, k_scale, v_scale, slot_mapping)}
+    _need(len(devs) == 1, "all tensors must be on one device")
+    with torch.cuda.device(k_pool.device):
+        _check(lib().pkv_kv_cache_write_fp8(
+            k_pool.data_ptr(), v_pool.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_scale.data_ptr(),
+            v_scale.data_ptr(), slot_mapping.data_ptr(), T, Hkv, D, BS, NB, DTYPE_CODES[dt],
+            _stream_handle(k_pool, stream)))

@@ -5,6 +5,7 @@
 // the device (and can be exercised on a machine with no GPU).
 #include "pkv.h"
 #include "pkv_blocks.h"
+#include "pkv_fp8.h"
 
 #include <atomic>
 #include <cmath>
@@ -182,12 +183,20 @@ int pkv_decode_plan(int32_t n_heads, int32_t n_kv_heads, int32_t block_size, int
   return ok();
 }
 
-int pkv_paged_attn_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
-                          const int32_t *block_tables, const int32_t *seq_lens, float scale,
-                          int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
-                          int32_t block_size, int32_t num_seqs, int32_t max_blocks_per_seq,
-                          int64_t num_blocks, int32_t dtype, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by the 16/32-bit and the FP8 decode entry points (fp8: pools hold
+// e4m3 codes, k_scale / v_scale are device float32 [n_kv_heads]).
+int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
+                const int32_t *block_tables, const int32_t *seq_lens, float scale, int32_t n_heads,
+                int32_t n_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_seqs,
+                int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype, void *stream, bool fp8,
+                const float *k_scale, const float *v_scale) {
   if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID, "unknown dtype %d", dtype);
+  if (fp8 && dtype == PKV_F32)
+    return fail(PKV_ERR_UNSUPPORTED, "FP8 pools need a float16 or bfloat16 query and output");
   if (num_seqs < 0 || num_seqs > 65535)
     return fail(PKV_ERR_INVALID, "num_seqs %d outside [0, 65535]", num_seqs);
   if (n_heads < 1 || n_kv_heads < 1)
@@ -211,6 +220,7 @@ int pkv_paged_attn_decode(void *out, const void *q, const void *k_pool, const vo
   if (num_seqs == 0) return ok();
   if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens)
     return fail(PKV_ERR_INVALID, "null array pointer");
+  if (fp8 && (!k_scale || !v_scale)) return fail(PKV_ERR_INVALID, "null scale pointer");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
     return fail(PKV_ERR_INVALID, "q, out, k_pool and v_pool must be 16-byte aligned");
 
@@ -232,6 +242,8 @@ int pkv_paged_attn_decode(void *out, const void *q, const void *k_pool, const vo
   a.block_shift = bshift;
   a.max_blocks = max_blocks_per_seq;
   a.num_blocks = num_blocks;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   plan(block_size, max_blocks_per_seq, &a.partition_tokens, &a.max_parts);
   if ((int64_t)num_seqs * a.max_parts * n_kv_heads * a.head_chunks > (int64_t)INT32_MAX)
     return fail(PKV_ERR_INVALID, "%d sequences x %d partitions x %d heads: too many workgroups",
@@ -250,8 +262,66 @@ int pkv_paged_attn_decode(void *out, const void *q, const void *k_pool, const vo
       if (rc != PKV_OK) return rc;
     }
   }
-  hipError_t e = pkv::launch_decode(static_cast<pkv::DType>(dtype), head_dim, a, st);
+  hipError_t e = fp8 ? pkv::launch_decode_fp8(static_cast<pkv::DType>(dtype), head_dim, a, st)
+                     : pkv::launch_decode(static_cast<pkv::DType>(dtype), head_dim, a, st);
   if (e != hipSuccess) return hip_fail(e, "paged decode launch");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_attn_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
+                          const int32_t *block_tables, const int32_t *seq_lens, float scale,
+                          int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t num_seqs, int32_t max_blocks_per_seq,
+                          int64_t num_blocks, int32_t dtype, void *stream) {
+  return decode_impl(out, q, k_pool, v_pool, block_tables, seq_lens, scale, n_heads, n_kv_heads, head_dim,
+                     block_size, num_seqs, max_blocks_per_seq, num_blocks, dtype, stream, false, nullptr,
+                     nullptr);
+}
+
+int pkv_paged_attn_decode_fp8(void *out, const void *q, const void *k_pool, const void *v_pool,
+                              const float *k_scale, const float *v_scale, const int32_t *block_tables,
+                              const int32_t *seq_lens, float scale, int32_t n_heads, int32_t n_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_seqs,
+                              int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype, void *stream) {
+  return decode_impl(out, q, k_pool, v_pool, block_tables, seq_lens, scale, n_heads, n_kv_heads, head_dim,
+                     block_size, num_seqs, max_blocks_per_seq, num_blocks, dtype, stream, true, k_scale,
+                     v_scale);
+}
+
+int pkv_kv_cache_write_fp8(void *k_pool, void *v_pool, const void *k_new, const void *v_new,
+                           const float *k_scale, const float *v_scale, const int32_t *slot_mapping,
+                           int32_t num_tokens, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                           int64_t num_blocks, int32_t dtype, void *stream) {
+  if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID, "unknown dtype %d", dtype);
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID, "num_tokens %d < 0", num_tokens);
+  if (n_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1)
+    return fail(PKV_ERR_INVALID, "n_kv_heads, head_dim, block_size, num_blocks must be >= 1");
+  if (head_dim % 16 != 0) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d is not a multiple of 16", head_dim);
+  if ((int64_t)n_kv_heads * (head_dim / 16) * 2 > (int64_t)INT32_MAX) return fail(PKV_ERR_INVALID, "row too large");
+  if (num_tokens == 0) return ok();
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping || !k_scale || !v_scale)
+    return fail(PKV_ERR_INVALID, "null pointer");
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(PKV_ERR_INVALID, "pools and new rows must be 16-byte aligned");
+  pkv::CacheWriteFp8Args a{};
+  a.k_pool = static_cast<uint8_t *>(k_pool);
+  a.v_pool = static_cast<uint8_t *>(v_pool);
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.n_kv_heads = n_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.num_slots = num_blocks * block_size;
+  hipError_t e = pkv::launch_cache_write_fp8(static_cast<pkv::DType>(dtype), a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fp8 cache write launch");
   return ok();
 }
 
@@ -293,12 +363,12 @@ int pkv_kv_cache_write(void *k_pool, void *v_pool, const void *k_new, const void
 int pkv_copy_blocks(void *k_pool, void *v_pool, const int32_t *pairs, int32_t num_pairs,
                     int32_t n_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
                     int32_t dtype, void *stream) {
-  if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID, "unknown dtype %d", dtype);
+  if (!valid_dtype(dtype) && dtype != PKV_FP8_E4M3) return fail(PKV_ERR_INVALID, "unknown dtype %d", dtype);
   if (num_pairs < 0) return fail(PKV_ERR_INVALID, "num_pairs %d < 0", num_pairs);
   if (n_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1)
     return fail(PKV_ERR_INVALID, "n_kv_heads, head_dim, block_size and num_blocks must be >= 1");
   const int64_t block_bytes = (int64_t)n_kv_heads * block_size * head_dim *
-                              pkv::dtype_bytes(static_cast<pkv::DType>(dtype));
+                              (dtype == PKV_FP8_E4M3 ? 1 : pkv::dtype_bytes(static_cast<pkv::DType>(dtype)));
   if (block_bytes % 16 != 0)
     return fail(PKV_ERR_UNSUPPORTED, "block of %lld bytes is not a multiple of 16", (long long)block_bytes);
   if (num_pairs == 0) return ok();

@@ -43,7 +43,110 @@ __global__ __launch_bounds__(kWriteThreads) void kv_cache_write_kernel(CacheWrit
   }
 }
 
+// --------------------------------------------------------------------------
+// FP8 (OCP e4m3) pools: each new row is quantized with its KV head's scale.
+// The value encoded is the float32 product x * (1 / scale) (both correctly
+// rounded), and the encoding rounds to the nearest e4m3 value, ties to the
+// even code, saturating at +-448; NaN stays NaN. KV-cache quantization is
+// one of the further KV optimisations the vLLM paper page lists; the format
+// and rounding are this library's (the pages fix none).
+// --------------------------------------------------------------------------
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t b = __float_as_uint(x);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t mag = b & 0x7fffffffu;
+  if (mag > 0x7f800000u) return sign | 0x7fu;   // NaN
+  if (mag >= 0x43e00000u) return sign | 0x7eu;  // |x| >= 448 (infinity too): saturate
+  const int e = (int)(mag >> 23);               // biased float32 exponent
+  const uint32_t m = mag & 0x7fffffu;
+  if (e >= 121) {                               // |x| >= 2^-6: normal e4m3
+    uint32_t r = m >> 20;
+    const uint32_t rem = m & 0xfffffu;
+    if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ++r;
+    const uint32_t code = ((uint32_t)(e - 120) << 3) + r;  // r == 8 carries into the exponent
+    return sign | (code > 0x7eu ? 0x7eu : code);
+  }
+  // below 2^-6: a multiple of the subnormal step 2^-9, |x| / 2^-9 = sig * 2^(e - 141)
+  const int sh = 141 - e;                       // >= 21
+  if (e == 0 || sh > 25) return sign;           // below half a step: zero
+  const uint32_t sig = (1u << 23) | m;
+  uint32_t q = sig >> sh;
+  const uint32_t rem = sig & ((1u << sh) - 1u), half = 1u << (sh - 1);
+  if (rem > half || (rem == half && (q & 1u))) ++q;
+  return sign | q;                              // 0 .. 8 (8 is the smallest normal, 0x08)
+}
+
+template <typename T> __device__ __forceinline__ float elem_to_float(T v) { return static_cast<float>(v); }
+
+// 16 consecutive input elements of one row -> 16 floats
+template <typename T> __device__ __forceinline__ void load16(const T *p, float *f) {
+  constexpr int kLoads = 16 * (int)sizeof(T) / 16;
+  constexpr int kPer = 16 / kLoads;
+  const u32x4_t *q = reinterpret_cast<const u32x4_t *>(p);
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const u32x4_t c = q[i];
+    const T *e = reinterpret_cast<const T *>(&c);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) f[i * kPer + j] = elem_to_float<T>(e[j]);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kWriteThreads) void kv_cache_write_fp8_kernel(CacheWriteFp8Args a) {
+  const int row_units = a.head_dim / 16;        // 16-element units per row
+  const int units = a.n_kv_heads * row_units;   // per token, per pool
+  for (int t = blockIdx.x; t < a.num_tokens; t += gridDim.x) {
+    for (int u = threadIdx.x; u < 2 * units; u += kWriteThreads) {
+      const bool is_v = u >= units;
+      const int uu = is_v ? u - units : u;
+      const int head = uu / row_units;
+      const int c = uu - head * row_units;
+      const T *src = static_cast<const T *>(is_v ? a.v_new : a.k_new) +
+                     ((int64_t)t * a.n_kv_heads + head) * a.head_dim + 16 * c;
+      int32_t slot32 = a.slot_mapping[t];
+      float f[16];
+      load16<T>(src, f);
+      const float sc = (is_v ? a.v_scale : a.k_scale)[head];
+      asm volatile("" : "+v"(slot32));
+      const int64_t slot = slot32;
+      if (slot < 0 || slot >= a.num_slots) continue;
+      const float inv = __fdiv_rn(1.0f, sc);
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        w[i] = f32_to_e4m3(__fmul_rn(f[4 * i], inv)) | (f32_to_e4m3(__fmul_rn(f[4 * i + 1], inv)) << 8) |
+               (f32_to_e4m3(__fmul_rn(f[4 * i + 2], inv)) << 16) |
+               (f32_to_e4m3(__fmul_rn(f[4 * i + 3], inv)) << 24);
+      }
+      const int64_t blk = slot / a.block_size;
+      const int64_t off = slot - blk * a.block_size;
+      uint8_t *dst = (is_v ? a.v_pool : a.k_pool) +
+                     ((blk * a.n_kv_heads + head) * a.block_size + off) * a.head_dim + 16 * c;
+      *reinterpret_cast<u32x4_t *>(dst) = u32x4_t{w[0], w[1], w[2], w[3]};
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_cache_write_fp8(DType in_dtype, const CacheWriteFp8Args &a, hipStream_t stream) {
+  const int grid = a.num_tokens < 65536 ? a.num_tokens : 65536;
+  switch (in_dtype) {
+    case DType::F32:
+      hipLaunchKernelGGL(kv_cache_write_fp8_kernel<float>, dim3(grid), dim3(kWriteThreads), 0, stream, a);
+      break;
+    case DType::F16:
+      hipLaunchKernelGGL(kv_cache_write_fp8_kernel<_Float16>, dim3(grid), dim3(kWriteThreads), 0, stream, a);
+      break;
+    case DType::BF16:
+      hipLaunchKernelGGL(kv_cache_write_fp8_kernel<__bf16>, dim3(grid), dim3(kWriteThreads), 0, stream, a);
+      break;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t stream) {
   const int grid = a.num_tokens < 65536 ? a.num_tokens : 65536;

@@ -161,6 +161,30 @@ __device__ __forceinline__ typename Pv<T>::v4 lds_read_tr(const void *p) {
   return __builtin_bit_cast(typename Pv<T>::v4, v);
 }
 
+// FP8 (OCP e4m3) storage: 16 codes -> 16 elements of T in two 16-byte chunks
+// (lo = elements 0..7, hi = 8..15). v_cvt_pk_f32_fp8 decodes two codes
+// exactly; every e4m3 value is exact in bf16 and fp16, so the float32 ->
+// 16-bit step loses nothing (bf16: the low 16 bits are zero).
+template <typename T> __device__ __forceinline__ uint32_t pack2_exact(float a, float b);
+template <> __device__ __forceinline__ uint32_t pack2_exact<__bf16>(float a, float b) {
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+}
+template <> __device__ __forceinline__ uint32_t pack2_exact<_Float16>(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+template <typename T> __device__ __forceinline__ void fp8x16_to(const u32x4_t &c, u32x4_t &lo, u32x4_t &hi) {
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[i], false);
+    const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[i], true);
+    w[2 * i] = pack2_exact<T>(f01[0], f01[1]);
+    w[2 * i + 1] = pack2_exact<T>(f23[0], f23[1]);
+  }
+  lo = u32x4_t{w[0], w[1], w[2], w[3]};
+  hi = u32x4_t{w[4], w[5], w[6], w[7]};
+}
+
 template <typename T, int D, int GT> struct Cfg {
   static constexpr int kEpc = Elem<T>::kPerChunk;        // elements per 16-byte chunk
   static constexpr int kCh = D / kEpc;                   // chunks per token row
@@ -318,10 +342,16 @@ __device__ __forceinline__ void locate_item(const ItemPlan &pl, int B, int j, in
 
 // One work item: query heads [hc GT, hc GT + GT) of KV head g (unit = g x
 // head chunk hc) over tokens [part P, part P + P) of sequence s.
-template <typename T, int D, int GT>
+// F8: the pools hold OCP e4m3 codes with one scale per KV head (k_scale,
+// v_scale); tiles are decoded to T on their way into LDS, k_scale is folded
+// into the score scale and v_scale into the output (partials included).
+template <typename T, int D, int GT, bool F8>
 __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int tid, int unit, int s, int part) {
   using C = Cfg<T, D, GT>;
-  constexpr int kL = C::kLoads;
+  static_assert(!F8 || C::kPvMfma, "FP8 pools need a 16-bit query type");
+  constexpr int kKvBytes = F8 ? 1 : (int)sizeof(T);     // bytes per stored element
+  constexpr int kL = kTileTokens * D * kKvBytes / (16 * 64);  // 16-byte loads per lane per K (or V) tile
+  constexpr int kChKV = D * kKvBytes / 16;               // 16-byte chunks per stored token row
   constexpr int kCh = C::kCh;
   constexpr int kEpc = C::kEpc;
   constexpr int kNW = C::kNW;
@@ -334,6 +364,12 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   const int head0 = g * a.group + hc * GT;
   const int nh = min(GT, a.group - hc * GT);
   T *out = static_cast<T *>(a.out);
+  float sl2 = a.scale_log2;  // scores in base-2 units
+  float vsc = 1.f;           // output scale
+  if constexpr (F8) {
+    sl2 *= a.k_scale[g];
+    vsc = a.v_scale[g];
+  }
 
   const int P = a.partition_tokens;
   const int start = part * P;
@@ -390,7 +426,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
       phys = 0;
     }
     return ((int64_t)phys * kv_stride_blk + (int64_t)g * a.block_size +
-            (tok & (a.block_size - 1))) * (D / kEpc);
+            (tok & (a.block_size - 1))) * kChKV;
   };
   const u32x4_t *kbase = static_cast<const u32x4_t *>(a.k_pool);
   const u32x4_t *vbase = static_cast<const u32x4_t *>(a.v_pool);
@@ -467,6 +503,24 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
     const bool partial = valid < kTileTokens;  // uniform
     // stage K (coalesced order -> swizzled LDS tile); the MFMA path also stages
     // V, zeroing rows past the sequence (0 * NaN would poison the sum)
+    if constexpr (F8) {
+      // each 16-byte load holds 16 codes of one token: two chunks of T
+      u32x4_t *vs = reinterpret_cast<u32x4_t *>(vst);
+#pragma unroll
+      for (int i = 0; i < kL; ++i) {
+        const int u = i * 64 + lane;
+        const int tr = u / kChKV;
+        const int c8 = u - tr * kChKV;
+        u32x4_t lo, hi;
+        fp8x16_to<T>(rg.k[i], lo, hi);
+        kst[kst_slot<kCh>(tr, 2 * c8)] = lo;
+        kst[kst_slot<kCh>(tr, 2 * c8 + 1)] = hi;
+        fp8x16_to<T>(rg.v[i], lo, hi);
+        if (partial && tr >= valid) lo = hi = u32x4_t{0u, 0u, 0u, 0u};
+        vs[tr * kCh + ((2 * c8) ^ vst_swz<kCh>(tr))] = lo;
+        vs[tr * kCh + ((2 * c8 + 1) ^ vst_swz<kCh>(tr))] = hi;
+      }
+    } else {
 #pragma unroll
     for (int i = 0; i < kL; ++i) {
       const int u = i * 64 + lane;
@@ -490,6 +544,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
         }
       }
     }
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -508,7 +563,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
     bool over = false;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      z[r] = tok_ok ? sc[r] * a.scale_log2 : -INFINITY;
+      z[r] = tok_ok ? sc[r] * sl2 : -INFINITY;
       over |= z[r] > m[r] + kLazy;
     }
     if (__builtin_amdgcn_ballot_w64(over) != 0) {  // uniform: raise the reference
@@ -695,6 +750,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
       den = fmaf(f, ml.y, den);
       num = fmaf(f, acc_of(w)[h * D + d], num);
     }
+    if constexpr (F8) num *= vsc;
     if (any_bad) {
       num = den = M = __builtin_nanf("");
     }
@@ -788,7 +844,7 @@ template <typename T, int D, int GT> constexpr int decode_waves_per_eu() {
   return (sizeof(T) == 2 || GT <= 4) ? 3 : 2;
 }
 
-template <typename T, int D, int GT>
+template <typename T, int D, int GT, bool F8>
 __global__ __launch_bounds__(kDecodeWaves * 64)
 __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT>()))) void paged_decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[Cfg<T, D, GT>::kSmem];
@@ -831,7 +887,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT>()))) void paged
     // held in registers through the tile loop.
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    decode_item<T, D, GT>(a, smem, tid, unit, s, part);
+    decode_item<T, D, GT, F8>(a, smem, tid, unit, s, part);
   }
 }
 
@@ -1010,7 +1066,7 @@ int device_cus() {
 // never more than the unit's largest possible item count.
 constexpr int kWgsPerSlot = 2;
 
-template <typename T, int D, int GT>
+template <typename T, int D, int GT, bool F8>
 hipError_t launch_t(const DecodeArgs &args, hipStream_t stream) {
   DecodeArgs a = args;
   const int64_t units = (int64_t)a.n_kv_heads * a.head_chunks;
@@ -1018,7 +1074,7 @@ hipError_t launch_t(const DecodeArgs &args, hipStream_t stream) {
   if (a.num_seqs <= kCompactSeqs) {
     static const int per_cu = [] {
       int nb = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, paged_decode_kernel<T, D, GT>, kDecodeWaves * 64, 0) !=
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, paged_decode_kernel<T, D, GT, F8>, kDecodeWaves * 64, 0) !=
               hipSuccess || nb <= 0)
         nb = 1;
       return nb;
@@ -1031,7 +1087,7 @@ hipError_t launch_t(const DecodeArgs &args, hipStream_t stream) {
     a.wgs_per_unit = (int32_t)max_items;
   }
   dim3 grid((unsigned)(units * a.wgs_per_unit), 1, 1);
-  hipLaunchKernelGGL((paged_decode_kernel<T, D, GT>), grid, dim3(kDecodeWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL((paged_decode_kernel<T, D, GT, F8>), grid, dim3(kDecodeWaves * 64), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.max_parts == 1 || a.arrivals != nullptr) return err;
   if (a.max_parts <= kFewParts) {
@@ -1045,23 +1101,23 @@ hipError_t launch_t(const DecodeArgs &args, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, bool F8>
 hipError_t launch_d(int gt, const DecodeArgs &a, hipStream_t stream) {
   switch (gt) {
-    case 1: return launch_t<T, D, 1>(a, stream);
-    case 2: return launch_t<T, D, 2>(a, stream);
-    case 4: return launch_t<T, D, 4>(a, stream);
-    case 8: return launch_t<T, D, 8>(a, stream);
-    case 16: return launch_t<T, D, 16>(a, stream);
+    case 1: return launch_t<T, D, 1, F8>(a, stream);
+    case 2: return launch_t<T, D, 2, F8>(a, stream);
+    case 4: return launch_t<T, D, 4, F8>(a, stream);
+    case 8: return launch_t<T, D, 8, F8>(a, stream);
+    case 16: return launch_t<T, D, 16, F8>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename T>
+template <typename T, bool F8>
 hipError_t launch_dt(int head_dim, int gt, const DecodeArgs &a, hipStream_t stream) {
   switch (head_dim) {
-    case 64: return launch_d<T, 64>(gt, a, stream);
-    case 128: return launch_d<T, 128>(gt, a, stream);
+    case 64: return launch_d<T, 64, F8>(gt, a, stream);
+    case 128: return launch_d<T, 128, F8>(gt, a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1090,11 +1146,20 @@ int decode_head_tile(int group) {
 hipError_t launch_decode(DType dt, int head_dim, const DecodeArgs &a, hipStream_t stream) {
   const int gt = decode_head_tile(a.group);
   switch (dt) {
-    case DType::F32: return launch_dt<float>(head_dim, gt, a, stream);
-    case DType::F16: return launch_dt<_Float16>(head_dim, gt, a, stream);
-    case DType::BF16: return launch_dt<__bf16>(head_dim, gt, a, stream);
+    case DType::F32: return launch_dt<float, false>(head_dim, gt, a, stream);
+    case DType::F16: return launch_dt<_Float16, false>(head_dim, gt, a, stream);
+    case DType::BF16: return launch_dt<__bf16, false>(head_dim, gt, a, stream);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_fp8(DType dt, int head_dim, const DecodeArgs &a, hipStream_t stream) {
+  const int gt = decode_head_tile(a.group);
+  switch (dt) {
+    case DType::F16: return launch_dt<_Float16, true>(head_dim, gt, a, stream);
+    case DType::BF16: return launch_dt<__bf16, true>(head_dim, gt, a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace pkv

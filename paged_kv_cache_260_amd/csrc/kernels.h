@@ -44,6 +44,9 @@ struct DecodeArgs {
   // set when the partitions of a sequence are merged by the last of them to
   // finish (max_parts <= kFusedMergeParts), null when a merge kernel runs.
   int32_t *arrivals;
+  // FP8 pools only: per-KV-head scales of the stored codes (null otherwise)
+  const float *k_scale;
+  const float *v_scale;
 };
 
 // Largest partition count merged inside the decode kernel; longer tables use
@@ -54,6 +57,10 @@ constexpr int kFusedMergeParts = 8;
 int decode_head_tile(int group);
 
 hipError_t launch_decode(DType dt, int head_dim, const DecodeArgs &a, hipStream_t stream);
+
+// Same over FP8 (OCP e4m3) pools with a.k_scale / a.v_scale; dt (query and
+// output) must be F16 or BF16.
+hipError_t launch_decode_fp8(DType dt, int head_dim, const DecodeArgs &a, hipStream_t stream);
 
 // Sets n int32 words to zero with a kernel (no memset node, so it may be captured).
 hipError_t launch_zero_i32(int32_t *p, int64_t n, hipStream_t stream);
@@ -72,6 +79,24 @@ struct CacheWriteArgs {
 };
 
 hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t stream);
+
+// Quantizing write into FP8 (OCP e4m3) pools: one float32 scale per KV head.
+struct CacheWriteFp8Args {
+  uint8_t *k_pool;
+  uint8_t *v_pool;
+  const void *k_new;       // [num_tokens, n_kv_heads, head_dim] of the input dtype
+  const void *v_new;
+  const float *k_scale;    // [n_kv_heads]
+  const float *v_scale;
+  const int32_t *slot_mapping;
+  int32_t num_tokens;
+  int32_t n_kv_heads;
+  int32_t head_dim;        // multiple of 16
+  int32_t block_size;
+  int64_t num_slots;
+};
+
+hipError_t launch_cache_write_fp8(DType in_dtype, const CacheWriteFp8Args &a, hipStream_t stream);
 
 struct CopyBlocksArgs {
   void *k_pool;
