@@ -170,6 +170,67 @@ def bench_copy_blocks(args, dev):
     }), flush=True)
 
 
+def bench_chunk(args, dev):
+    """Multi-token chunk attention on two workloads:
+    - speculative verification: the GQA batch-128 shapes, each sequence
+      scoring its last 4 tokens (HBM-bound, like decode);
+    - chunked prefill: 4 sequences of 4 096 cached tokens, each scoring a
+      512-token chunk (the last 512 tokens): a dense causal contraction
+      (MFMA-bound in principle)."""
+    results = {}
+    cases = [("spec_verify_qlen4", workloads.make(3), 4),
+             ("prefill_chunk512", workloads.build(name="prefill", rng=np.random.default_rng(2607),
+                                                  seq_lens=np.full(4, 4096), n_heads=32, n_kv_heads=8,
+                                                  head_dim=128, block_size=16, dtype=torch.bfloat16), 512)]
+    for name, w, qlen in cases:
+        qlens = np.minimum(qlen, w.seq_lens).astype(np.int64)
+        qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+        T = int(qsl[-1])
+        q = torch.randn(T, w.n_heads, w.head_dim, device=dev).to(w.dtype)
+        out = torch.empty_like(q)
+        bt = torch.from_numpy(w.block_tables).to(dev)
+        sl = torch.from_numpy(w.seq_lens).to(dev)
+        qs = torch.from_numpy(qsl).to(dev)
+        R = max(3, math.ceil(3 * MALL_BYTES / (2 * w.k_pool.numel() * w.elem_bytes)))
+        kps = [w.k_pool.to(dev) for _ in range(R)]
+        vps = [w.v_pool.to(dev) for _ in range(R)]
+        call = lambda r: _lib.paged_attn_chunk(out, q, kps[r], vps[r], bt, sl, qs, w.scale, w.n_heads,
+                                               w.n_kv_heads, w.head_dim, w.block_size, int(qlens.max()))
+        for i in range(args.warmup):
+            call(i % R)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.steps):
+            call(i % R)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        kv = accounting.decode_kv_bytes(w.seq_lens, w.n_kv_heads, w.head_dim, w.elem_bytes)
+        qo = 2 * T * w.n_heads * w.head_dim * w.elem_bytes
+        # visible (query row, token) pairs: token i of a chunk of n sees L - n + i + 1 tokens
+        pairs = int(sum(int(n) * (int(L) - int(n)) + int(n) * (int(n) + 1) // 2 for n, L in zip(qlens, w.seq_lens)))
+        flops = 4 * pairs * w.n_heads * w.head_dim
+        results[name] = {"qlen": qlen, "batch": w.num_seqs, "query_tokens": T, "us": round(us, 3),
+                         "GBps": round((kv + qo) / (us * 1e-6) / 1e9, 1),
+                         "TFLOPs": round(flops / (us * 1e-6) / 1e12, 2), "bytes": kv + qo, "flops": flops}
+        del kps, vps
+        torch.cuda.empty_cache()
+    sv, pf = results["spec_verify_qlen4"], results["prefill_chunk512"]
+    print(json.dumps({
+        "metric": "chunk attention: effective HBM GB/s (speculative verify) and TFLOP/s (prefill chunk)",
+        "value": sv["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "paged chunk attention, causal inside the chunk", **results},
+        "roofline": {"bound": "hbm", "achieved": sv["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(sv["GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "paged_chunk_kernel (speculative verify)", "algorithmic_bytes": sv["bytes"]},
+        "roofline_prefill": {"bound": "mfma", "achieved": pf["TFLOPs"], "peak": 2500.0, "unit": "TFLOP/s",
+                             "frac": round(pf["TFLOPs"] / 2500.0, 4), "kernel": "paged_chunk_kernel (prefill chunk)",
+                             "algorithmic_flops": pf["flops"]},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,7 +243,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
-    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks"],
+    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "chunk"],
                     help="decode = the hot-path step (default); copy_blocks = copy-on-write block copy")
     ap.add_argument("--kv", default="native", choices=["native", "fp8"],
                     help="KV pool storage: the query dtype (default) or FP8 e4m3 codes with per-head scales")
@@ -200,6 +261,9 @@ def main():
     _lib.lib()
     if args.op == "copy_blocks":
         bench_copy_blocks(args, dev)
+        return
+    if args.op == "chunk":
+        bench_chunk(args, dev)
         return
     _lib.set_partition_tokens(args.partition)
 

@@ -136,3 +136,52 @@ def paged_attn_decode_partitioned(q, k_pool, v_pool, block_tables, seq_lens, sca
                 out[s, h] = num / den
                 partials[(s, h)] = parts
     return out, partials
+
+
+def paged_attn_chunk(q, k_pool, v_pool, block_tables, seq_lens, query_start_loc, scale, n_heads,
+                     n_kv_heads, head_dim, block_size) -> np.ndarray:
+    """Attention of a chunk of new query tokens per sequence, causal inside the chunk.
+
+    Several new tokens of one sequence are scored in one pass. Sources:
+      - Sarathi-Serve chunked prefill (PagedAttention notes page): a long
+        prompt's prefill is cut into chunks interleaved with decodes.
+      - Speculative decoding (vLLM notes page): the target model scores K
+        draft tokens at once.
+      - Continuous batching (vLLM notes page, scheduling section): sequences
+        are packed into one flat token list; position indices and the
+        attention mask keep each token on its own sequence.
+
+    Readings: ``q`` is the packed ``[T, H, D]`` chunk rows; the rows of
+    sequence ``s`` are ``query_start_loc[s] .. query_start_loc[s + 1] - 1``.
+    These ``n_s`` tokens are the last ``n_s`` of the sequence's ``L_s`` cached
+    tokens (their K/V are already written). Token ``i`` of the chunk sits at
+    position ``p = L_s - n_s + i`` and, as in autoregressive decoding, sees
+    every cached token at positions ``0 .. p``. ``n_s = 1`` is one decode
+    step; ``n_s = L_s`` is a whole causal prefill.
+    """
+    q = np.asarray(q)
+    block_tables = np.asarray(block_tables)
+    qsl = [int(x) for x in np.asarray(query_start_loc).reshape(-1)]
+    seq_lens = [int(x) for x in np.asarray(seq_lens).reshape(-1)]
+    B = len(seq_lens)
+    if len(qsl) != B + 1 or any(qsl[s + 1] < qsl[s] for s in range(B)):
+        raise ValueError("query_start_loc must be [B + 1], nondecreasing")
+    if q.shape != (qsl[-1], n_heads, head_dim):
+        raise ValueError(f"q shape {q.shape}")
+    G = n_heads // n_kv_heads
+    out = np.zeros((qsl[-1], n_heads, head_dim), dtype=np.float64)
+    for s, L in enumerate(seq_lens):
+        n = qsl[s + 1] - qsl[s]
+        if n == 0:
+            continue
+        if n > L or L > block_tables.shape[1] * block_size:
+            raise ValueError(f"sequence {s}: {n} query tokens, {L} cached")
+        for g in range(n_kv_heads):
+            K = gather_tokens(k_pool, block_tables[s], g, L, block_size)
+            V = gather_tokens(v_pool, block_tables[s], g, L, block_size)
+            for i in range(n):
+                p = L - n + i
+                rows = q[qsl[s] + i, g * G:(g + 1) * G]
+                P = attention_weights(rows, K[:p + 1], scale)   # [G, p + 1]
+                out[qsl[s] + i, g * G:(g + 1) * G] = P @ V[:p + 1]
+    return out

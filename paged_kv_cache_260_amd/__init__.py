@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     kv_cache_write,
     kv_cache_write_fp8,
     last_error,
+    paged_attn_chunk,
     paged_attn_decode,
     paged_attn_decode_fp8,
     release_workspace,
@@ -29,6 +30,7 @@ __all__ = [
     "BlockManager",
     "copy_blocks",
     "paged_attn_decode_fp8",
+    "paged_attn_chunk",
     "kv_cache_write_fp8",
     "kv_cache_write",
     "decode_plan",

@@ -1,5 +1,5 @@
 """ctypes binding of ``libpkv.so`` (``include/pkv.h``, ``include/pkv_blocks.h``,
-``include/pkv_fp8.h``).
+``include/pkv_fp8.h``, ``include/pkv_chunk.h``).
 
 Argument marshalling only: shapes, dtypes and devices of torch tensors are
 checked and turned into the raw pointers and sizes of the C ABI, together
@@ -50,6 +50,9 @@ _SIGNATURES = {
     "pkv_bm_build_tables": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp]),
     "pkv_bm_free_queue": (ctypes.c_int, [_vp, _vp, _i64]),
     "pkv_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
+    # multi-token chunk attention (pkv_chunk.h)
+    "pkv_paged_attn_chunk": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32, _i32, _i32,
+                                            _i32, _i32, _i64, _i32, _i32, _vp]),
     # FP8 (e4m3) KV cache (pkv_fp8.h)
     "pkv_paged_attn_decode_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32,
                                                  _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
@@ -357,3 +360,33 @@ def kv_cache_write_fp8(k_pool: torch.Tensor, v_pool: torch.Tensor, k_new: torch.
             k_pool.data_ptr(), v_pool.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_scale.data_ptr(),
             v_scale.data_ptr(), slot_mapping.data_ptr(), T, Hkv, D, BS, NB, DTYPE_CODES[dt],
             _stream_handle(k_pool, stream)))
+
+
+def paged_attn_chunk(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                     block_tables: torch.Tensor, seq_lens: torch.Tensor, query_start_loc: torch.Tensor,
+                     scale: float, n_heads: int, n_kv_heads: int, head_dim: int, block_size: int,
+                     max_query_len: int, stream=None) -> torch.Tensor:
+    """Causal attention of the last ``n_s`` tokens of each sequence (packed ``q``/``out`` ``[T, H, D]``,
+    ``query_start_loc`` int32 ``[B + 1]``; the chunk's K/V already in the pools)."""
+    dt = q.dtype
+    _need(dt in (torch.float16, torch.bfloat16), f"chunk attention needs fp16/bf16, got {dt}")
+    for name, t in (("out", out), ("q", q), ("k_pool", k_pool), ("v_pool", v_pool)):
+        _dev_tensor(t, name, dt)
+    for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens), ("query_start_loc", query_start_loc)):
+        _dev_tensor(t, name, torch.int32)
+    B = seq_lens.shape[0]
+    _need(q.dim() == 3 and q.shape[1:] == (n_heads, head_dim) and out.shape == q.shape, "q/out must be [T, H, D]")
+    _need(k_pool.dim() == 4 and k_pool.shape[1:] == (n_kv_heads, block_size, head_dim),
+          "k_pool must be [NB, Hkv, BS, D]")
+    _need(v_pool.shape == k_pool.shape, "v_pool must match k_pool")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B, MB]")
+    _need(query_start_loc.shape == (B + 1,), "query_start_loc must be [B + 1]")
+    devs = {t.device for t in (out, q, k_pool, v_pool, block_tables, seq_lens, query_start_loc)}
+    _need(len(devs) == 1, "all tensors must be on one device")
+    with torch.cuda.device(q.device):
+        _check(lib().pkv_paged_attn_chunk(
+            out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), block_tables.data_ptr(),
+            seq_lens.data_ptr(), query_start_loc.data_ptr(), float(scale), n_heads, n_kv_heads, head_dim,
+            block_size, B, block_tables.shape[1], k_pool.shape[0], int(max_query_len), DTYPE_CODES[dt],
+            _stream_handle(q, stream)))
+    return out

@@ -6,6 +6,7 @@
 #include "pkv.h"
 #include "pkv_blocks.h"
 #include "pkv_fp8.h"
+#include "pkv_chunk.h"
 
 #include <atomic>
 #include <cmath>
@@ -290,6 +291,59 @@ int pkv_paged_attn_decode_fp8(void *out, const void *q, const void *k_pool, cons
   return decode_impl(out, q, k_pool, v_pool, block_tables, seq_lens, scale, n_heads, n_kv_heads, head_dim,
                      block_size, num_seqs, max_blocks_per_seq, num_blocks, dtype, stream, true, k_scale,
                      v_scale);
+}
+
+int pkv_paged_attn_chunk(void *out, const void *q, const void *k_pool, const void *v_pool,
+                         const int32_t *block_tables, const int32_t *seq_lens, const int32_t *query_start_loc,
+                         float scale, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t num_seqs, int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_query_len,
+                         int32_t dtype, void *stream) {
+  if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID, "unknown dtype %d", dtype);
+  if (dtype == PKV_F32) return fail(PKV_ERR_UNSUPPORTED, "chunk attention is built for float16 and bfloat16");
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID, "num_seqs %d < 0", num_seqs);
+  if (n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "n_heads %d must be a positive multiple of n_kv_heads %d", n_heads, n_kv_heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d: built for 64 and 128", head_dim);
+  const int bshift = log2_exact(block_size);
+  if (block_size < 16 || block_size > 128 || bshift < 0)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d: built for 16, 32, 64, 128", block_size);
+  if (max_blocks_per_seq < 1 || num_blocks < 1)
+    return fail(PKV_ERR_INVALID, "max_blocks_per_seq and num_blocks must be >= 1");
+  if ((int64_t)max_blocks_per_seq * block_size > (int64_t)INT32_MAX)
+    return fail(PKV_ERR_INVALID, "max_blocks_per_seq * block_size exceeds int32");
+  if (max_query_len < 0) return fail(PKV_ERR_INVALID, "max_query_len %d < 0", max_query_len);
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID, "scale is not finite");
+  const int group = n_heads / n_kv_heads;
+  const int64_t row_blocks = ((int64_t)max_query_len * group + 15) / 16;
+  if (num_seqs == 0 || row_blocks == 0) return ok();
+  if ((int64_t)n_kv_heads * num_seqs * row_blocks > (int64_t)INT32_MAX)
+    return fail(PKV_ERR_INVALID, "too many work items");
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens || !query_start_loc)
+    return fail(PKV_ERR_INVALID, "null array pointer");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(PKV_ERR_INVALID, "q, out, k_pool and v_pool must be 16-byte aligned");
+  pkv::ChunkArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.query_start_loc = query_start_loc;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.num_seqs = num_seqs;
+  a.n_heads = n_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.group = group;
+  a.block_size = block_size;
+  a.block_shift = bshift;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.row_blocks = (int32_t)row_blocks;
+  hipError_t e = pkv::launch_chunk(static_cast<pkv::DType>(dtype), head_dim, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "chunk attention launch");
+  return ok();
 }
 
 int pkv_kv_cache_write_fp8(void *k_pool, void *v_pool, const void *k_new, const void *v_new,

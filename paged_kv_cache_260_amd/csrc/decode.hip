@@ -36,6 +36,7 @@
 //   5. 16-bit storage: P (as hi + lo halves) and the V tile are read back
 //      transposed with ds_read_b64_tr_b16 and multiplied on
 //      v_mfma_f32_16x16x16; fp32 storage accumulates P * V on the VALU.
+#include "attn_common.h"
 #include "kernels.h"
 
 #include <math.h>
@@ -45,145 +46,7 @@
 namespace pkv {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-// 16 bytes as a native vector (HIP's u32x4_t is a union struct whose copies
-// become memcpy and keep values out of registers).
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-template <typename T> struct Elem;
-template <> struct Elem<float> { static constexpr int kPerChunk = 4; };
-template <> struct Elem<_Float16> { static constexpr int kPerChunk = 8; };
-template <> struct Elem<__bf16> { static constexpr int kPerChunk = 8; };
-
-// ---------------------------------------------------------------------------
-// element conversions (16-byte chunk -> fp32)
-// ---------------------------------------------------------------------------
-template <typename T> __device__ __forceinline__ void chunk_to_float(const u32x4_t &c, float *f);
-
-template <> __device__ __forceinline__ void chunk_to_float<__bf16>(const u32x4_t &c, float *f) {
-  const uint32_t w[4] = {c[0], c[1], c[2], c[3]};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(w[i] << 16);
-    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
-}
-
-template <> __device__ __forceinline__ void chunk_to_float<_Float16>(const u32x4_t &c, float *f) {
-  const f16x8_t h = __builtin_bit_cast(f16x8_t, c);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) f[i] = static_cast<float>(h[i]);
-}
-
-template <> __device__ __forceinline__ void chunk_to_float<float>(const u32x4_t &c, float *f) {
-  f[0] = __uint_as_float(c[0]);
-  f[1] = __uint_as_float(c[1]);
-  f[2] = __uint_as_float(c[2]);
-  f[3] = __uint_as_float(c[3]);
-}
-
-// ---------------------------------------------------------------------------
-// one MFMA step over a 16-byte chunk per lane: C += A(16 x k) * B(k x 16)
-// ---------------------------------------------------------------------------
-template <typename T> __device__ __forceinline__ f32x4_t mfma_chunk(u32x4_t a, u32x4_t b, f32x4_t c);
-
-template <> __device__ __forceinline__ f32x4_t mfma_chunk<__bf16>(u32x4_t a, u32x4_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
-template <> __device__ __forceinline__ f32x4_t mfma_chunk<_Float16>(u32x4_t a, u32x4_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
-                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-}
-
-template <> __device__ __forceinline__ f32x4_t mfma_chunk<float>(u32x4_t a, u32x4_t b, f32x4_t c) {
-  // 16x16x4 fp32: lane (kg, n) supplies k = kg; the four words are four k-steps.
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[i]), __uint_as_float(b[i]), c, 0, 0, 0);
-  return c;
-}
-
-// ---------------------------------------------------------------------------
-// 16-lane (DPP row) reductions; every lane of the row receives the result
-// ---------------------------------------------------------------------------
-template <int kCtrl> __device__ __forceinline__ float dpp_f(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
-}
-// row_ror:n has control 0x120 + n; rotations by 8, 4, 2, 1 cover the row.
-__device__ __forceinline__ float row_max16(float x) {
-  x = fmaxf(x, dpp_f<0x128>(x));
-  x = fmaxf(x, dpp_f<0x124>(x));
-  x = fmaxf(x, dpp_f<0x122>(x));
-  x = fmaxf(x, dpp_f<0x121>(x));
-  return x;
-}
-__device__ __forceinline__ float row_sum16(float x) {
-  x += dpp_f<0x128>(x);
-  x += dpp_f<0x124>(x);
-  x += dpp_f<0x122>(x);
-  x += dpp_f<0x121>(x);
-  return x;
-}
-
-__device__ __forceinline__ float readlane_f(float x, int lane) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
-}
-
-template <typename T> struct Pv;  // 4-element operand of the 16x16x16 MFMA
-template <> struct Pv<__bf16> {
-  typedef __bf16 v4 __attribute__((ext_vector_type(4)));
-  static __device__ __forceinline__ f32x4_t mfma(v4 a, v4 b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-  }
-};
-template <> struct Pv<_Float16> {
-  typedef _Float16 v4 __attribute__((ext_vector_type(4)));
-  static __device__ __forceinline__ f32x4_t mfma(v4 a, v4 b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-  }
-};
-
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
-
-// ds_read_b64_tr_b16: within each 16-lane group, output lane j receives
-// element (j % 4) of the 8-byte chunks addressed by lanes j / 4 + 4 r,
-// r = 0..3 -- one column of a 4-row block per lane.
-template <typename T>
-__device__ __forceinline__ typename Pv<T>::v4 lds_read_tr(const void *p) {
-  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_i16x4_t *)(__attribute__((address_space(3))) void *)(p));
-  return __builtin_bit_cast(typename Pv<T>::v4, v);
-}
-
-// FP8 (OCP e4m3) storage: 16 codes -> 16 elements of T in two 16-byte chunks
-// (lo = elements 0..7, hi = 8..15). v_cvt_pk_f32_fp8 decodes two codes
-// exactly; every e4m3 value is exact in bf16 and fp16, so the float32 ->
-// 16-bit step loses nothing (bf16: the low 16 bits are zero).
-template <typename T> __device__ __forceinline__ uint32_t pack2_exact(float a, float b);
-template <> __device__ __forceinline__ uint32_t pack2_exact<__bf16>(float a, float b) {
-  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
-}
-template <> __device__ __forceinline__ uint32_t pack2_exact<_Float16>(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
-}
-template <typename T> __device__ __forceinline__ void fp8x16_to(const u32x4_t &c, u32x4_t &lo, u32x4_t &hi) {
-  uint32_t w[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[i], false);
-    const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[i], true);
-    w[2 * i] = pack2_exact<T>(f01[0], f01[1]);
-    w[2 * i + 1] = pack2_exact<T>(f23[0], f23[1]);
-  }
-  lo = u32x4_t{w[0], w[1], w[2], w[3]};
-  hi = u32x4_t{w[4], w[5], w[6], w[7]};
-}
+using namespace attn;
 
 template <typename T, int D, int GT> struct Cfg {
   static constexpr int kEpc = Elem<T>::kPerChunk;        // elements per 16-byte chunk
@@ -219,20 +82,6 @@ template <typename T, int D, int GT> struct Cfg {
   static_assert(!kPvMfma || kCh == 8 || kCh == 16, "MFMA P*V path: 8 or 16 chunks per row");
   static_assert(GT >= 1 && GT <= 16, "head tile");
 };
-
-// Swizzled 16-byte slot of chunk `ch` of token `tr` in a staged K tile: the
-// 16 tokens read together in one MFMA step land in 16 distinct bank groups.
-template <int kCh> __device__ __forceinline__ int kst_slot(int tr, int ch) {
-  const int sw = (kCh >= 16 ? tr : (tr >> 1)) & (kCh - 1);
-  return tr * kCh + (ch ^ sw);
-}
-// XOR pattern of a staged V tile. Transposed reads of one 16-dim block touch
-// two adjacent chunks (2b, 2b+1) of 4 consecutive tokens per 16-lane group;
-// an even pattern that differs across those tokens puts the 8 chunks in 8
-// distinct bank groups (and keeps chunk pairs together: (2b + h) ^ sw = (2b ^ sw) + h).
-template <int kCh> __device__ __forceinline__ int vst_swz(int tr) {
-  return kCh >= 16 ? (2 * tr) & 15 : 2 * ((tr >> 1) & 3);
-}
 
 // Longest-first item order for batches of up to kCompactSeqs sequences.
 // A sequence of L tokens has n = ceil(L / P) partitions: n - 1 full ones and

@@ -58,6 +58,29 @@ int decode_head_tile(int group);
 
 hipError_t launch_decode(DType dt, int head_dim, const DecodeArgs &a, hipStream_t stream);
 
+// Multi-token (chunk) attention: the last n_s tokens of each sequence, causal.
+struct ChunkArgs {
+  void *out;                       // [T, n_heads, head_dim]
+  const void *q;                   // [T, n_heads, head_dim]
+  const void *k_pool;
+  const void *v_pool;
+  const int32_t *block_tables;
+  const int32_t *seq_lens;
+  const int32_t *query_start_loc;  // [num_seqs + 1]
+  float scale_log2;
+  int32_t num_seqs;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t group;
+  int32_t block_size;
+  int32_t block_shift;
+  int32_t max_blocks;
+  int64_t num_blocks;
+  int32_t row_blocks;              // ceil(max_query_len * group / 16)
+};
+
+hipError_t launch_chunk(DType dt, int head_dim, const ChunkArgs &a, hipStream_t stream);
+
 // Same over FP8 (OCP e4m3) pools with a.k_scale / a.v_scale; dt (query and
 // output) must be F16 or BF16.
 hipError_t launch_decode_fp8(DType dt, int head_dim, const DecodeArgs &a, hipStream_t stream);
