@@ -72,6 +72,14 @@ std::atomic<int32_t> g_partition_override{0};
 // shorter partitions lose to per-workgroup startup cost.)
 constexpr int64_t kAutoPartition = 1024;
 
+// Chunk attention takes the decode kernel's work items while a chunk fills at
+// most this many 16-row blocks per KV head (chunk length x query heads per KV
+// head <= 64 rows); longer chunks go to the chunk kernel.
+#ifndef PKV_CHUNK_ROWS_MAX_BLOCKS
+#define PKV_CHUNK_ROWS_MAX_BLOCKS 4
+#endif
+constexpr int64_t kChunkRowsMaxBlocks = PKV_CHUNK_ROWS_MAX_BLOCKS;
+
 void plan(int32_t block_size, int32_t max_blocks, int32_t *ptok, int32_t *nparts) {
   const int64_t max_tokens = (int64_t)max_blocks * block_size;
   int64_t p = g_partition_override.load();
@@ -323,6 +331,48 @@ int pkv_paged_attn_chunk(void *out, const void *q, const void *k_pool, const voi
     return fail(PKV_ERR_INVALID, "null array pointer");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
     return fail(PKV_ERR_INVALID, "q, out, k_pool and v_pool must be 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (row_blocks <= kChunkRowsMaxBlocks) {
+    // short chunks (speculative verification, small chunked-prefill pieces):
+    // the decode kernel's split, longest-first work items with 16 chunk rows each
+    pkv::DecodeArgs a{};
+    a.out = out;
+    a.q = q;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.query_start_loc = query_start_loc;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    a.num_seqs = num_seqs;
+    a.n_heads = n_heads;
+    a.n_kv_heads = n_kv_heads;
+    a.group = group;
+    a.head_chunks = (int32_t)row_blocks;
+    a.block_size = block_size;
+    a.block_shift = bshift;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_blocks = num_blocks;
+    plan(block_size, max_blocks_per_seq, &a.partition_tokens, &a.max_parts);
+    const int64_t items = (int64_t)num_seqs * n_kv_heads * row_blocks;
+    if (items * a.max_parts > (int64_t)INT32_MAX) return fail(PKV_ERR_INVALID, "too many work items");
+    if (a.max_parts > 1) {
+      const size_t rows = (size_t)items * 16 * a.max_parts;
+      const size_t acc_bytes = rows * head_dim * sizeof(float);
+      void *ws = nullptr;
+      int rc = get_workspace(st, acc_bytes + rows * sizeof(float2), &ws);
+      if (rc != PKV_OK) return rc;
+      a.part_acc = static_cast<float *>(ws);
+      a.part_ml = reinterpret_cast<float2 *>(static_cast<char *>(ws) + acc_bytes);
+      if (a.max_parts <= pkv::kFusedMergeParts) {
+        rc = get_arrivals(st, items, &a.arrivals);
+        if (rc != PKV_OK) return rc;
+      }
+    }
+    hipError_t e = pkv::launch_chunk_rows(static_cast<pkv::DType>(dtype), head_dim, false, a, st);
+    if (e != hipSuccess) return hip_fail(e, "chunk attention launch");
+    return ok();
+  }
   pkv::ChunkArgs a{};
   a.out = out;
   a.q = q;
@@ -341,7 +391,7 @@ int pkv_paged_attn_chunk(void *out, const void *q, const void *k_pool, const voi
   a.max_blocks = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.row_blocks = (int32_t)row_blocks;
-  hipError_t e = pkv::launch_chunk(static_cast<pkv::DType>(dtype), head_dim, a, static_cast<hipStream_t>(stream));
+  hipError_t e = pkv::launch_chunk(static_cast<pkv::DType>(dtype), head_dim, a, st);
   if (e != hipSuccess) return hip_fail(e, "chunk attention launch");
   return ok();
 }

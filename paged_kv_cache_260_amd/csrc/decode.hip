@@ -194,10 +194,17 @@ __device__ __forceinline__ void locate_item(const ItemPlan &pl, int B, int j, in
 // F8: the pools hold OCP e4m3 codes with one scale per KV head (k_scale,
 // v_scale); tiles are decoded to T on their way into LDS, k_scale is folded
 // into the score scale and v_scale into the output (partials included).
-template <typename T, int D, int GT, bool F8>
+// CH (chunk rows, GT = 16): the sequence's last n = qsl[s+1] - qsl[s] tokens
+// are queries, and the item's 16 rows are (chunk token, query head of g)
+// pairs, token-major from row 16 hc (unit = g x row block hc): row r is
+// token r / G, head g G + r % G. Chunk token i sits at position L - n + i and
+// sees tokens 0 .. L - n + i only, so each row carries its own last visible
+// token; the item's context ends after its last row's position.
+template <typename T, int D, int GT, bool F8, bool CH>
 __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int tid, int unit, int s, int part) {
   using C = Cfg<T, D, GT>;
   static_assert(!F8 || C::kPvMfma, "FP8 pools need a 16-bit query type");
+  static_assert(!CH || (GT == 16 && C::kPvMfma), "chunk rows: 16-row tiles, 16-bit types");
   constexpr int kKvBytes = F8 ? 1 : (int)sizeof(T);     // bytes per stored element
   constexpr int kL = kTileTokens * D * kKvBytes / (16 * 64);  // 16-byte loads per lane per K (or V) tile
   constexpr int kChKV = D * kKvBytes / 16;               // 16-byte chunks per stored token row
@@ -210,9 +217,31 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   const int g = unit / a.head_chunks;
   const int hc = unit - g * a.head_chunks;
   const int H = a.n_heads;
-  const int head0 = g * a.group + hc * GT;
-  const int nh = min(GT, a.group - hc * GT);
+  const int G = a.group;
+  const int head0 = g * G + hc * GT;
   T *out = static_cast<T *>(a.out);
+  // chunk rows: first query token of the sequence, chunk length, first row
+  int q0 = 0, nq = 0;
+  const int row0 = hc * GT;
+  if constexpr (CH) {
+    q0 = a.query_start_loc[s];
+    nq = a.query_start_loc[s + 1] - q0;
+  }
+  const int nh = CH ? max(0, min(GT, nq * G - row0)) : min(GT, G - hc * GT);
+  // output (and query) row of item row i
+  auto row_index = [&](int i) -> int64_t {
+    if constexpr (CH) {
+      const int r = row0 + i;
+      return (int64_t)(q0 + r / G) * H + g * G + r % G;
+    } else {
+      return (int64_t)s * H + head0 + i;
+    }
+  };
+  // partial-result row of item row i (split items)
+  auto part_row = [&](int i) -> int64_t {
+    if constexpr (CH) return ((int64_t)s * units + unit) * GT + i;
+    else return (int64_t)s * H + head0 + i;
+  };
   float sl2 = a.scale_log2;  // scores in base-2 units
   float vsc = 1.f;           // output scale
   if constexpr (F8) {
@@ -234,7 +263,15 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   // block (rows past nh are zero)
   constexpr int kQPer = (C::kQChunks + kNW * 64 - 1) / (kNW * 64);
   u32x4_t qv[kQPer];
-  {
+  if constexpr (CH) {
+#pragma unroll
+    for (int i = 0; i < kQPer; ++i) {
+      const int u = tid + i * kNW * 64;
+      qv[i] = u32x4_t{0u, 0u, 0u, 0u};
+      if (u < C::kQChunks && u / kCh < nh)
+        qv[i] = reinterpret_cast<const u32x4_t *>(static_cast<const T *>(a.q) + row_index(u / kCh) * D)[u % kCh];
+    }
+  } else {
     const u32x4_t *qblk = reinterpret_cast<const u32x4_t *>(static_cast<const T *>(a.q) +
                                                             ((int64_t)s * H + head0) * D);
 #pragma unroll
@@ -245,18 +282,28 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
     }
   }
   const int L = a.seq_lens[s];
-  const bool bad_len = L < 0 || (int64_t)L > (int64_t)a.max_blocks * a.block_size;
+  if (CH && nh == 0) return;  // no query rows (empty chunk, or past its last row)
+  const bool bad_len = L < 0 || (int64_t)L > (int64_t)a.max_blocks * a.block_size || (CH && (L < nq || q0 < 0));
   if (bad_len || L == 0) {
     if (part == 0) {
       const float v = bad_len ? __builtin_nanf("") : 0.f;
       for (int i = tid; i < nh * D; i += kNW * 64)
-        out[((int64_t)s * H + head0) * D + i] = static_cast<T>(v);
+        out[row_index(i / D) * D + i % D] = static_cast<T>(v);
     }
     return;
   }
-  if (start >= L) return;
-  const int end = min(L, start + P);
-  const int nparts = (L + P - 1) / P;
+  // tokens the item's rows may see: [0, ctx)
+  const int ctx = CH ? L - nq + (row0 + nh - 1) / G + 1 : L;
+  // last visible token of rows 4 kg + r of this lane (chunk rows)
+  int lim[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = 4 * (lane >> 4) + r;
+    lim[r] = CH && i < nh ? L - nq + (row0 + i) / G : (CH ? -1 : INT32_MAX);
+  }
+  if (start >= ctx) return;
+  const int end = min(ctx, start + P);
+  const int nparts = (ctx + P - 1) / P;
 
   // Block ids of the partition (at most 64 table entries): lane i of btv holds
   // entry jb + i. They are read back with v_readlane, so the per-tile lookup
@@ -406,13 +453,17 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
       sc = mfma_chunk<T>(n < GT ? qs[kst_slot<kCh>(n, kg + 4 * c)] : u32x4_t{0u, 0u, 0u, 0u},
                          kst[kst_slot<kCh>(n, kg + 4 * c)], sc);
 
-    // scores in base-2 units; tokens past the sequence get -inf
+    // scores in base-2 units; tokens past the sequence (chunk rows: past the
+    // row's position) get -inf
     const bool tok_ok = n < valid;
     float z[4];
     bool over = false;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      z[r] = tok_ok ? sc[r] * sl2 : -INFINITY;
+      if constexpr (CH)
+        z[r] = tok_ok && ti * kTileTokens + n <= lim[r] ? sc[r] * sl2 : -INFINITY;
+      else
+        z[r] = tok_ok ? sc[r] * sl2 : -INFINITY;
       over |= z[r] > m[r] + kLazy;
     }
     if (__builtin_amdgcn_ballot_w64(over) != 0) {  // uniform: raise the reference
@@ -421,6 +472,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
       for (int r = 0; r < 4; ++r) {
         const float mn = fmaxf(m[r], row_max16(z[r]));
         alpha[r] = __builtin_amdgcn_exp2f(m[r] - mn);  // 0 on the first tile (m = -inf)
+        // chunk rows may have seen nothing yet (mn = -inf): keep them empty
+        if constexpr (CH) alpha[r] = mn == -INFINITY ? 1.f : alpha[r];
         m[r] = mn;
         l[r] *= alpha[r];
       }
@@ -442,6 +495,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       p[r] = __builtin_amdgcn_exp2f(z[r] - m[r]);
+      if constexpr (CH) p[r] = z[r] == -INFINITY ? 0.f : p[r];  // also when m = -inf
       l[r] += p[r];
     }
 
@@ -606,11 +660,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
     rM[k] = M;
     rnum[k] = num;
     rden[k] = den;
-    const int64_t row = (int64_t)s * H + head0 + h;
     if (nparts == 1) {
-      out[row * D + d] = static_cast<T>(num / den);
+      out[row_index(h) * D + d] = static_cast<T>(num / den);
     } else {
-      const int64_t pi = row * a.max_parts + part;
+      const int64_t pi = part_row(h) * a.max_parts + part;
       if (!fused) {
         a.part_acc[pi * D + d] = num;
         if (d == 0) a.part_ml[pi] = make_float2(M, den);
@@ -652,7 +705,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
     if (idx >= nh * D) continue;
     const int h = idx / D;
     const int d = idx - h * D;
-    const int64_t row = (int64_t)s * H + head0 + h;
+    const int64_t prow = part_row(h);
     float2 oml[kFusedMergeParts];
     float ox[kFusedMergeParts];
 #pragma unroll
@@ -660,7 +713,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
       oml[p] = make_float2(-INFINITY, 0.f);
       ox[p] = 0.f;
       if (p < nparts && p != part) {
-        const int64_t pi = row * a.max_parts + p;
+        const int64_t pi = prow * a.max_parts + p;
         oml[p] = __builtin_bit_cast(
             float2, __hip_atomic_load(reinterpret_cast<unsigned long long *>(a.part_ml + pi),
                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
@@ -682,7 +735,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
       den = fmaf(f, oml[p].y, den);
       num = fmaf(f, ox[p], num);
     }
-    out[row * D + d] = static_cast<T>(bad ? __builtin_nanf("") : num / den);
+    out[row_index(h) * D + d] = static_cast<T>(bad ? __builtin_nanf("") : num / den);
   }
 }
 
@@ -693,7 +746,7 @@ template <typename T, int D, int GT> constexpr int decode_waves_per_eu() {
   return (sizeof(T) == 2 || GT <= 4) ? 3 : 2;
 }
 
-template <typename T, int D, int GT, bool F8>
+template <typename T, int D, int GT, bool F8, bool CH>
 __global__ __launch_bounds__(kDecodeWaves * 64)
 __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT>()))) void paged_decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[Cfg<T, D, GT>::kSmem];
@@ -736,7 +789,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT>()))) void paged
     // held in registers through the tile loop.
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    decode_item<T, D, GT, F8>(a, smem, tid, unit, s, part);
+    decode_item<T, D, GT, F8, CH>(a, smem, tid, unit, s, part);
   }
 }
 
@@ -898,6 +951,57 @@ __global__ __launch_bounds__(kMergeThreads) void paged_decode_merge_few_kernel(D
   }
 }
 
+// Merge of split chunk-row items when a table allows more partitions than the
+// in-kernel merge takes: one workgroup per (sequence, unit); thread t folds
+// the partitions of output elements t, t + 256, ... of the item's rows with
+// the same online rescaling (partitions that saw none of a row's tokens hold
+// m = -inf and are skipped).
+constexpr int kChunkReduceThreads = 256;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kChunkReduceThreads) void paged_chunk_reduce_kernel(DecodeArgs a) {
+  constexpr int kRows = 16;
+  const int units = a.n_kv_heads * a.head_chunks;
+  const int s = (int)(blockIdx.x / (unsigned)units);
+  const int unit = (int)(blockIdx.x - (unsigned)s * units);
+  const int g = unit / a.head_chunks;
+  const int row0 = (unit - g * a.head_chunks) * kRows;
+  const int G = a.group;
+  const int q0 = a.query_start_loc[s];
+  const int nq = a.query_start_loc[s + 1] - q0;
+  const int L = a.seq_lens[s];
+  const int nh = max(0, min(kRows, nq * G - row0));
+  if (nh == 0 || L < nq || q0 < 0 || (int64_t)L > (int64_t)a.max_blocks * a.block_size) return;
+  const int ctx = L - nq + (row0 + nh - 1) / G + 1;
+  const int P = a.partition_tokens;
+  const int nparts = (ctx + P - 1) / P;
+  if (nparts <= 1) return;  // written by the attention kernel
+  for (int idx = threadIdx.x; idx < nh * D; idx += kChunkReduceThreads) {
+    const int i = idx / D;
+    const int d = idx - i * D;
+    const int64_t prow = ((int64_t)s * units + unit) * kRows + i;
+    const float2 *ml = a.part_ml + prow * a.max_parts;
+    const float *acc = a.part_acc + prow * a.max_parts * D + d;
+    float M = -INFINITY, num = 0.f, den = 0.f;
+    bool bad = false;
+    for (int p = 0; p < nparts; ++p) {
+      const float2 v = ml[p];
+      const float x = acc[(int64_t)p * D];
+      bad |= v.x != v.x;
+      if (!(v.x > -INFINITY)) continue;
+      const float mn = fmaxf(M, v.x);
+      const float f0 = __builtin_amdgcn_exp2f(M - mn);  // 0 while M = -inf
+      const float f = __builtin_amdgcn_exp2f(v.x - mn);
+      den = fmaf(f, v.y, den * f0);
+      num = fmaf(f, x, num * f0);
+      M = mn;
+    }
+    const int r = row0 + i;
+    static_cast<T *>(a.out)[((int64_t)(q0 + r / G) * a.n_heads + g * G + r % G) * D + d] =
+        static_cast<T>(bad ? __builtin_nanf("") : num / den);
+  }
+}
+
 // Compute units of the current device (cached per device).
 int device_cus() {
   static std::atomic<int> cache[64];
@@ -915,7 +1019,7 @@ int device_cus() {
 // never more than the unit's largest possible item count.
 constexpr int kWgsPerSlot = 2;
 
-template <typename T, int D, int GT, bool F8>
+template <typename T, int D, int GT, bool F8, bool CH = false>
 hipError_t launch_t(const DecodeArgs &args, hipStream_t stream) {
   DecodeArgs a = args;
   const int64_t units = (int64_t)a.n_kv_heads * a.head_chunks;
@@ -923,7 +1027,7 @@ hipError_t launch_t(const DecodeArgs &args, hipStream_t stream) {
   if (a.num_seqs <= kCompactSeqs) {
     static const int per_cu = [] {
       int nb = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, paged_decode_kernel<T, D, GT, F8>, kDecodeWaves * 64, 0) !=
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, paged_decode_kernel<T, D, GT, F8, CH>, kDecodeWaves * 64, 0) !=
               hipSuccess || nb <= 0)
         nb = 1;
       return nb;
@@ -936,9 +1040,14 @@ hipError_t launch_t(const DecodeArgs &args, hipStream_t stream) {
     a.wgs_per_unit = (int32_t)max_items;
   }
   dim3 grid((unsigned)(units * a.wgs_per_unit), 1, 1);
-  hipLaunchKernelGGL((paged_decode_kernel<T, D, GT, F8>), grid, dim3(kDecodeWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL((paged_decode_kernel<T, D, GT, F8, CH>), grid, dim3(kDecodeWaves * 64), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.max_parts == 1 || a.arrivals != nullptr) return err;
+  if constexpr (CH) {
+    hipLaunchKernelGGL((paged_chunk_reduce_kernel<T, D>), dim3((unsigned)(units * a.num_seqs)),
+                       dim3(kChunkReduceThreads), 0, stream, a);
+    return hipGetLastError();
+  }
   if (a.max_parts <= kFewParts) {
     const int hblocks = (a.n_heads + merge_heads_per_wg<D>() - 1) / merge_heads_per_wg<D>();
     hipLaunchKernelGGL((paged_decode_merge_few_kernel<T, D>), dim3((unsigned)(a.num_seqs * hblocks)),
@@ -948,6 +1057,15 @@ hipError_t launch_t(const DecodeArgs &args, hipStream_t stream) {
     hipLaunchKernelGGL((paged_decode_reduce_kernel<T, D>), rgrid, dim3(kReduceThreads), 0, stream, a);
   }
   return hipGetLastError();
+}
+
+template <typename T, bool F8>
+hipError_t launch_rows_t(int head_dim, const DecodeArgs &a, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_t<T, 64, 16, F8, true>(a, stream);
+    case 128: return launch_t<T, 128, 16, F8, true>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <typename T, int D, bool F8>
@@ -1000,6 +1118,16 @@ hipError_t launch_decode(DType dt, int head_dim, const DecodeArgs &a, hipStream_
     case DType::BF16: return launch_dt<__bf16, false>(head_dim, gt, a, stream);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_rows(DType dt, int head_dim, bool fp8, const DecodeArgs &a, hipStream_t stream) {
+  switch (dt) {
+    case DType::F16: return fp8 ? launch_rows_t<_Float16, true>(head_dim, a, stream)
+                                : launch_rows_t<_Float16, false>(head_dim, a, stream);
+    case DType::BF16: return fp8 ? launch_rows_t<__bf16, true>(head_dim, a, stream)
+                                 : launch_rows_t<__bf16, false>(head_dim, a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_decode_fp8(DType dt, int head_dim, const DecodeArgs &a, hipStream_t stream) {

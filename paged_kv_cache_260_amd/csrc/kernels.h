@@ -47,6 +47,10 @@ struct DecodeArgs {
   // FP8 pools only: per-KV-head scales of the stored codes (null otherwise)
   const float *k_scale;
   const float *v_scale;
+  // Chunk rows only (launch_chunk_rows): [num_seqs + 1] offsets of each
+  // sequence's query tokens; head_chunks then counts 16-row blocks per KV head
+  // and partial rows are indexed per item: ((s * units + unit) * 16 + row).
+  const int32_t *query_start_loc;
 };
 
 // Largest partition count merged inside the decode kernel; longer tables use
@@ -80,6 +84,11 @@ struct ChunkArgs {
 };
 
 hipError_t launch_chunk(DType dt, int head_dim, const ChunkArgs &a, hipStream_t stream);
+
+// Chunk attention on the decode kernel's work items (16 rows of (token, head)
+// pairs per item, split along the sequence and merged like decode); dt is
+// F16 or BF16; fp8 selects e4m3 pools with a.k_scale / a.v_scale.
+hipError_t launch_chunk_rows(DType dt, int head_dim, bool fp8, const DecodeArgs &a, hipStream_t stream);
 
 // Same over FP8 (OCP e4m3) pools with a.k_scale / a.v_scale; dt (query and
 // output) must be F16 or BF16.

@@ -1,6 +1,12 @@
 """GPU parity of multi-token (chunk) attention through the C ABI against the
 fp64 oracle: decode-sized chunks, speculative-verification chunks, prefill
-chunks and whole-sequence prefill, mixed batches, and invalid lengths."""
+chunks and whole-sequence prefill, mixed batches, and invalid lengths.
+
+Short chunks (at most 64 rows of (token, query head) per KV head) run on the
+split, longest-first work items of the decode kernel; the tests force short
+partitions so that rows whose every visible token lies before a partition,
+the in-kernel merge (at most 8 partitions) and the separate merge (more) are
+all reached. Longer chunks run on the chunk kernel."""
 import sys
 
 import numpy as np
@@ -19,6 +25,13 @@ def _need_gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     _lib.lib()
+
+
+@pytest.fixture(autouse=True)
+def _auto_partition():
+    _lib.set_partition_tokens(0)
+    yield
+    _lib.set_partition_tokens(0)
 
 
 def say(msg):
@@ -119,3 +132,61 @@ def test_invalid_lengths_give_nan_rows():
     good = np.concatenate([np.arange(qsl[0], qsl[1]), np.arange(qsl[2], qsl[3])])
     ref = run_oracle(w, q, qsl)
     assert np.abs(out[good] - ref[good]).max() <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("partition", [16, 48, 192, 1024])
+@pytest.mark.parametrize("H,Hkv,D,BS,qmax,dtype", [(32, 8, 128, 16, 16, torch.bfloat16),
+                                                   (8, 8, 64, 32, 64, torch.float16),
+                                                   (64, 8, 128, 16, 3, torch.bfloat16),
+                                                   (12, 4, 64, 16, 5, torch.float16)])
+def test_short_chunks_split(H, Hkv, D, BS, qmax, dtype, partition):
+    """Short chunks (up to 64 rows per KV head) with the sequence split into
+    partitions of 16 to 1024 tokens: rows straddle tokens (G = 8, G = 3),
+    whole-sequence chunks sit beside decode steps and empty chunks."""
+    _lib.set_partition_tokens(partition)
+    say(f"short chunks H={H} Hkv={Hkv} D={D} BS={BS} qmax={qmax} partition={partition}")
+    w = workloads.random_case(300 + qmax + BS, num_seqs=9, n_heads=H, n_kv_heads=Hkv, head_dim=D, block_size=BS,
+                              dtype=dtype, max_len=2600, min_len=1, poison=True)
+    rng = np.random.default_rng(qmax)
+    qlens = np.minimum(rng.integers(1, qmax + 1, size=w.num_seqs), w.seq_lens)
+    qlens[2] = 0
+    qlens[5] = min(qmax, int(w.seq_lens[5]))
+    q, qsl = chunk_inputs(w, qlens, qmax + partition)
+    out = run_gpu(w, q, qsl)
+    err = max_abs_err(out, run_oracle(w, q, qsl))
+    say(f"  max abs err {err:.3e}")
+    assert err <= TOL[dtype]
+
+
+def test_short_chunks_whole_small_sequences():
+    """Sequences no longer than their chunk (whole causal prefill of a few
+    tokens) on the short-chunk path, with 16-token partitions."""
+    _lib.set_partition_tokens(16)
+    w = workloads.random_case(51, num_seqs=6, n_heads=16, n_kv_heads=16, head_dim=128, block_size=16,
+                              dtype=torch.bfloat16, max_len=60, min_len=1, poison=True)
+    qlens = np.minimum(w.seq_lens, 60)
+    q, qsl = chunk_inputs(w, qlens, 8)
+    out = run_gpu(w, q, qsl)
+    assert max_abs_err(out, run_oracle(w, q, qsl)) <= TOL[w.dtype]
+
+
+def test_short_chunks_long_context():
+    """4 draft tokens over contexts of 9 000 to 30 000 tokens: 1024-token
+    partitions, more than the in-kernel merge takes."""
+    say("short chunks, long context")
+    w = workloads.build(name="long", rng=np.random.default_rng(61), seq_lens=[30000, 9000, 17000],
+                        n_heads=16, n_kv_heads=4, head_dim=128, block_size=16, dtype=torch.bfloat16)
+    q, qsl = chunk_inputs(w, [4, 4, 1], 9)
+    out = run_gpu(w, q, qsl)
+    err = max_abs_err(out, run_oracle(w, q, qsl))
+    say(f"  max abs err {err:.3e}")
+    assert err <= TOL[w.dtype]
+
+
+def test_short_chunks_large_batch():
+    """300 sequences (past the longest-first planner's batch limit) with 2-token chunks."""
+    w = workloads.random_case(71, num_seqs=300, n_heads=8, n_kv_heads=2, head_dim=64, block_size=16,
+                              dtype=torch.float16, max_len=700, min_len=2, poison=True)
+    q, qsl = chunk_inputs(w, np.full(w.num_seqs, 2), 10)
+    out = run_gpu(w, q, qsl)
+    assert max_abs_err(out, run_oracle(w, q, qsl)) <= TOL[w.dtype]
