@@ -231,6 +231,60 @@ def bench_chunk(args, dev):
     }), flush=True)
 
 
+def bench_shared_prefix(args, dev):
+    """Decode of the 16-prompt x 4-sample fp16 workload (1024 shared prompt
+    tokens per prompt) two ways: plain decode, which reads the shared blocks
+    once per sample, and the shared-prefix call, which reads them once per
+    prompt. Bandwidth is counted on the compulsory bytes (each physical block
+    once, plus Q and O)."""
+    w = workloads.make(5)
+    gs, pl, mg = _lib.shared_prefix_groups(w.block_tables, w.seq_lens, w.block_size)
+    uniq = accounting.unique_kv_tokens(w.seq_lens, w.block_tables, w.block_size)
+    comp = uniq * w.n_kv_heads * w.head_dim * 2 * w.elem_bytes + accounting.decode_qo_bytes(
+        w.num_seqs, w.n_heads, w.head_dim, w.elem_bytes)
+    logical = accounting.decode_compulsory_bytes(w.seq_lens, w.n_heads, w.n_kv_heads, w.head_dim, w.elem_bytes)
+    q = w.q.to(dev)
+    out = torch.empty_like(q)
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    sl = torch.from_numpy(w.seq_lens).to(dev)
+    gsd = torch.from_numpy(gs).to(dev)
+    pld = torch.from_numpy(pl).to(dev)
+    R = max(3, math.ceil(3 * MALL_BYTES / (2 * w.k_pool.numel() * w.elem_bytes)))
+    kps = [w.k_pool.to(dev) for _ in range(R)]
+    vps = [w.v_pool.to(dev) for _ in range(R)]
+    calls = {
+        "shared_prefix": lambda r: _lib.paged_attn_decode_shared_prefix(
+            out, q, kps[r], vps[r], bt, sl, pld, gsd, w.scale, w.n_heads, w.n_kv_heads, w.head_dim, w.block_size, mg),
+        "plain_decode": lambda r: _lib.paged_attn_decode(out, q, kps[r], vps[r], bt, sl, w.scale, w.n_heads,
+                                                         w.n_kv_heads, w.head_dim, w.block_size),
+    }
+    res = {}
+    for name, call in calls.items():
+        for i in range(args.warmup):
+            call(i % R)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.steps):
+            call(i % R)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        res[name] = {"us": round(us, 3), "GBps_compulsory": round(comp / (us * 1e-6) / 1e9, 1)}
+    sp = res["shared_prefix"]
+    print(json.dumps({
+        "metric": "shared-prefix decode: compulsory-byte HBM GB/s", "value": sp["GBps_compulsory"], "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": workloads.CONFIG_NAMES[5], "groups": int(len(gs) - 1), "max_group_size": int(mg),
+                   "compulsory_bytes": comp, "logical_bytes": logical, **res},
+        "roofline": {"bound": "hbm", "achieved": sp["GBps_compulsory"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(sp["GBps_compulsory"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "paged_attn_decode_shared_prefix call (prefix + suffix kernels)",
+                     "algorithmic_bytes": comp},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,7 +297,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
-    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "chunk"],
+    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "chunk", "shared_prefix"],
                     help="decode = the hot-path step (default); copy_blocks = copy-on-write block copy")
     ap.add_argument("--kv", default="native", choices=["native", "fp8"],
                     help="KV pool storage: the query dtype (default) or FP8 e4m3 codes with per-head scales")
@@ -264,6 +318,9 @@ def main():
         return
     if args.op == "chunk":
         bench_chunk(args, dev)
+        return
+    if args.op == "shared_prefix":
+        bench_shared_prefix(args, dev)
         return
     _lib.set_partition_tokens(args.partition)
 

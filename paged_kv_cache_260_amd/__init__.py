@@ -3,10 +3,13 @@ slot-mapped cache write, as hand-written HIP kernels behind a C ABI
 (``include/pkv.h``).
 
 ``paged_attn_decode`` and ``kv_cache_write`` take torch tensors on the GPU and
-call the HIP library; ``BlockManager`` (host) hands out pool blocks with
-reference-counted sharing and copy-on-write, whose copies ``copy_blocks`` runs
-on the GPU; the library is loaded on first use and a missing build
-raises. ``workloads`` builds seeded synthetic inputs; ``accounting`` holds the
+call the HIP library; ``paged_attn_chunk`` scores several new tokens per
+sequence (causal), ``paged_attn_decode_shared_prefix`` reads a prompt prefix
+shared by a group of sequences once per group (``shared_prefix_groups``
+derives the groups from host tables), and the ``_fp8`` variants work on e4m3
+pools. ``BlockManager`` (host) hands out pool blocks with reference-counted
+sharing and copy-on-write, whose copies ``copy_blocks`` runs on the GPU; the
+library is loaded on first use and a missing build raises. ``workloads`` builds seeded synthetic inputs; ``accounting`` holds the
 byte counts used to turn kernel time into bandwidth.
 """
 from ._lib import (  # noqa: F401
@@ -20,8 +23,10 @@ from ._lib import (  # noqa: F401
     paged_attn_chunk,
     paged_attn_decode,
     paged_attn_decode_fp8,
+    paged_attn_decode_shared_prefix,
     release_workspace,
     set_partition_tokens,
+    shared_prefix_groups,
     version,
 )
 
@@ -31,6 +36,8 @@ __all__ = [
     "copy_blocks",
     "paged_attn_decode_fp8",
     "paged_attn_chunk",
+    "paged_attn_decode_shared_prefix",
+    "shared_prefix_groups",
     "kv_cache_write_fp8",
     "kv_cache_write",
     "decode_plan",

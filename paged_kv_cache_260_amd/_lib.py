@@ -53,6 +53,11 @@ _SIGNATURES = {
     # multi-token chunk attention (pkv_chunk.h)
     "pkv_paged_attn_chunk": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _i64, _i32, _i32, _vp]),
+    # shared-prefix decode (pkv_shared_prefix.h)
+    "pkv_paged_attn_decode_shared_prefix": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32,
+                                                           _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
+                                                           _i32, _vp]),
+    "pkv_shared_prefix_groups": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     # FP8 (e4m3) KV cache (pkv_fp8.h)
     "pkv_paged_attn_decode_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32,
                                                  _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
@@ -390,3 +395,55 @@ def paged_attn_chunk(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v
             block_size, B, block_tables.shape[1], k_pool.shape[0], int(max_query_len), DTYPE_CODES[dt],
             _stream_handle(q, stream)))
     return out
+
+
+def paged_attn_decode_shared_prefix(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
+                                    v_pool: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                                    prefix_lens: torch.Tensor, group_start: torch.Tensor, scale: float,
+                                    n_heads: int, n_kv_heads: int, head_dim: int, block_size: int,
+                                    max_group_size: int, stream=None) -> torch.Tensor:
+    """Decode of a batch whose consecutive sequence groups share a prompt prefix
+    (``group_start`` int32 ``[G + 1]``, ``prefix_lens`` int32 ``[B]``); same
+    result as :func:`paged_attn_decode`."""
+    dt = q.dtype
+    _need(dt in (torch.float16, torch.bfloat16), f"shared-prefix decode needs fp16/bf16, got {dt}")
+    for name, t in (("out", out), ("q", q), ("k_pool", k_pool), ("v_pool", v_pool)):
+        _dev_tensor(t, name, dt)
+    for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens), ("prefix_lens", prefix_lens),
+                    ("group_start", group_start)):
+        _dev_tensor(t, name, torch.int32)
+    B = seq_lens.shape[0]
+    _need(q.shape == (B, n_heads, head_dim) and out.shape == q.shape, "q/out must be [B, H, D]")
+    _need(k_pool.dim() == 4 and k_pool.shape[1:] == (n_kv_heads, block_size, head_dim),
+          "k_pool must be [NB, Hkv, BS, D]")
+    _need(v_pool.shape == k_pool.shape, "v_pool must match k_pool")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B, MB]")
+    _need(prefix_lens.shape == (B,), "prefix_lens must be [B]")
+    _need(group_start.dim() == 1 and group_start.shape[0] >= 2, "group_start must be [G + 1]")
+    devs = {t.device for t in (out, q, k_pool, v_pool, block_tables, seq_lens, prefix_lens, group_start)}
+    _need(len(devs) == 1, "all tensors must be on one device")
+    with torch.cuda.device(q.device):
+        _check(lib().pkv_paged_attn_decode_shared_prefix(
+            out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), block_tables.data_ptr(),
+            seq_lens.data_ptr(), prefix_lens.data_ptr(), group_start.data_ptr(), float(scale), n_heads,
+            n_kv_heads, head_dim, block_size, B, group_start.shape[0] - 1, int(max_group_size),
+            block_tables.shape[1], k_pool.shape[0], DTYPE_CODES[dt], _stream_handle(q, stream)))
+    return out
+
+
+def shared_prefix_groups(block_tables, seq_lens, block_size: int):
+    """Sharing description from host tables (numpy int32 ``[B, MB]`` and ``[B]``):
+    ``(group_start [G + 1], prefix_lens [B], max_group_size)`` as numpy int32."""
+    import numpy as np
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    _need(bt.ndim == 2 and sl.shape == (bt.shape[0],), "block_tables [B, MB] and seq_lens [B]")
+    B = bt.shape[0]
+    gs = np.zeros(B + 1, dtype=np.int32)
+    pl = np.zeros(B, dtype=np.int32)
+    ng = ctypes.c_int32(0)
+    mg = ctypes.c_int32(0)
+    _check(lib().pkv_shared_prefix_groups(bt.ctypes.data, sl.ctypes.data, B, max(1, bt.shape[1]), int(block_size),
+                                          gs.ctypes.data, pl.ctypes.data, ctypes.addressof(ng),
+                                          ctypes.addressof(mg)))
+    return gs[:ng.value + 1].copy() if B else np.zeros(1, np.int32), pl, mg.value

@@ -7,7 +7,9 @@
 #include "pkv_blocks.h"
 #include "pkv_fp8.h"
 #include "pkv_chunk.h"
+#include "pkv_shared_prefix.h"
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -393,6 +395,168 @@ int pkv_paged_attn_chunk(void *out, const void *q, const void *k_pool, const voi
   a.row_blocks = (int32_t)row_blocks;
   hipError_t e = pkv::launch_chunk(static_cast<pkv::DType>(dtype), head_dim, a, st);
   if (e != hipSuccess) return hip_fail(e, "chunk attention launch");
+  return ok();
+}
+
+int pkv_paged_attn_decode_shared_prefix(void *out, const void *q, const void *k_pool, const void *v_pool,
+                                        const int32_t *block_tables, const int32_t *seq_lens,
+                                        const int32_t *prefix_lens, const int32_t *group_start, float scale,
+                                        int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                                        int32_t num_seqs, int32_t num_groups, int32_t max_group_size,
+                                        int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
+                                        void *stream) {
+  if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID, "unknown dtype %d", dtype);
+  if (dtype == PKV_F32)
+    return fail(PKV_ERR_UNSUPPORTED, "shared-prefix decode is built for float16 and bfloat16");
+  if (num_seqs < 0 || num_seqs > 65535)
+    return fail(PKV_ERR_INVALID, "num_seqs %d outside [0, 65535]", num_seqs);
+  if (n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "n_heads %d must be a positive multiple of n_kv_heads %d", n_heads, n_kv_heads);
+  const int group = n_heads / n_kv_heads;
+  if (group > 256) return fail(PKV_ERR_UNSUPPORTED, "n_heads / n_kv_heads = %d > 256", group);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d: built for 64 and 128", head_dim);
+  const int bshift = log2_exact(block_size);
+  if (block_size < 16 || block_size > 128 || bshift < 0)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d: built for 16, 32, 64, 128", block_size);
+  if (max_blocks_per_seq < 1 || num_blocks < 1)
+    return fail(PKV_ERR_INVALID, "max_blocks_per_seq and num_blocks must be >= 1");
+  if ((int64_t)max_blocks_per_seq * block_size > (int64_t)INT32_MAX)
+    return fail(PKV_ERR_INVALID, "max_blocks_per_seq * block_size exceeds int32");
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID, "scale is not finite");
+  if (num_seqs == 0) return ok();
+  if (num_groups < 1 || num_groups > num_seqs)
+    return fail(PKV_ERR_INVALID, "num_groups %d outside [1, num_seqs = %d]", num_groups, num_seqs);
+  if (max_group_size < 1 || max_group_size > num_seqs)
+    return fail(PKV_ERR_INVALID, "max_group_size %d outside [1, num_seqs = %d]", max_group_size, num_seqs);
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens || !prefix_lens || !group_start)
+    return fail(PKV_ERR_INVALID, "null array pointer");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(PKV_ERR_INVALID, "q, out, k_pool and v_pool must be 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  // suffix launch: plain decode items over each sequence's private tokens
+  pkv::DecodeArgs suf{};
+  suf.out = out;
+  suf.q = q;
+  suf.k_pool = k_pool;
+  suf.v_pool = v_pool;
+  suf.block_tables = block_tables;
+  suf.seq_lens = seq_lens;
+  suf.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  suf.num_seqs = num_seqs;
+  suf.n_heads = n_heads;
+  suf.n_kv_heads = n_kv_heads;
+  suf.group = group;
+  const int gt = pkv::decode_head_tile(group);
+  suf.head_chunks = (group + gt - 1) / gt;
+  suf.block_size = block_size;
+  suf.block_shift = bshift;
+  suf.max_blocks = max_blocks_per_seq;
+  suf.num_blocks = num_blocks;
+  suf.prefix_lens = prefix_lens;
+  suf.member_seqs = num_seqs;
+  plan(block_size, max_blocks_per_seq, &suf.partition_tokens, &suf.max_parts);
+
+  const int64_t max_tokens = (int64_t)max_blocks_per_seq * block_size;
+  const int64_t slots = 2 * (int64_t)pkv::kDecodeWgsPerCu * pkv::device_cus();
+
+  // One launch for both kinds of work item when every group's rows fit one
+  // 16-row block per KV head and the partial slots per (sequence, head) fit
+  // the in-kernel merge.
+  if (group <= 16 && (group & (group - 1)) == 0 && (int64_t)max_group_size * group <= 16) {
+    int64_t p_pre = suf.partition_tokens, n_pre = suf.max_parts;
+    if (g_partition_override.load() <= 0) {
+      // shortest prefix partition whose count fits the slots the private
+      // parts leave; the kernel lengthens it to the longest private part
+      const int64_t want = pkv::kFusedMergeParts - suf.max_parts;
+      if (want >= 1) {
+        p_pre = (max_tokens + want - 1) / want;
+        p_pre = p_pre > block_size ? (p_pre + block_size - 1) / block_size * block_size : (p_pre + 15) / 16 * 16;
+        p_pre = std::min<int64_t>(p_pre, (int64_t)pkv::kMaxPartitionBlocks * block_size);
+        n_pre = (max_tokens + p_pre - 1) / p_pre;
+      } else {
+        n_pre = pkv::kFusedMergeParts;  // no room: two launches
+      }
+    }
+    if (n_pre + suf.max_parts <= pkv::kFusedMergeParts) {
+      pkv::DecodeArgs a = suf;
+      a.num_seqs = num_groups + num_seqs;  // entities
+      a.num_groups = num_groups;
+      a.query_start_loc = group_start;
+      a.head_chunks = 1;
+      a.prefix_partition_tokens = (int32_t)p_pre;
+      a.prefix_partition_fixed = g_partition_override.load() > 0;
+      a.max_parts = (int32_t)(n_pre + suf.max_parts);  // slot stride
+      const size_t rows = (size_t)num_seqs * n_heads * a.max_parts;
+      const size_t acc_bytes = rows * head_dim * sizeof(float);
+      void *ws = nullptr;
+      int rc = get_workspace(st, acc_bytes + rows * sizeof(float2), &ws);
+      if (rc != PKV_OK) return rc;
+      a.part_acc = static_cast<float *>(ws);
+      a.part_ml = reinterpret_cast<float2 *>(static_cast<char *>(ws) + acc_bytes);
+      rc = get_arrivals(st, (int64_t)num_seqs * n_kv_heads, &a.arrivals);
+      if (rc != PKV_OK) return rc;
+      hipError_t e = pkv::launch_shared_fused(static_cast<pkv::DType>(dtype), head_dim, a, st);
+      if (e != hipSuccess) return hip_fail(e, "shared-prefix decode launch");
+      return ok();
+    }
+  }
+
+  // prefix launch: rows of (member, head) over each group's shared prefix
+  pkv::DecodeArgs pre = suf;
+  pre.query_start_loc = group_start;
+  pre.num_seqs = num_groups;
+  const int64_t row_blocks = ((int64_t)max_group_size * group + 15) / 16;
+  pre.head_chunks = (int32_t)row_blocks;
+  const int64_t pre_items = (int64_t)num_groups * n_kv_heads * row_blocks;
+  // Few groups give few prefix items, each walking a long prefix: split the
+  // prefix so that the items fill about two rounds of the chip's resident
+  // workgroups (at most kFusedMergeParts partitions, whole blocks, at most
+  // kMaxPartitionBlocks blocks each, at least one 16-token tile).
+  if (g_partition_override.load() <= 0) {
+    const int64_t want = std::min<int64_t>(pkv::kFusedMergeParts, std::max<int64_t>(1, (slots + pre_items - 1) / pre_items));
+    int64_t p = (max_tokens + want - 1) / want;
+    p = p > block_size ? (p + block_size - 1) / block_size * block_size : (p + 15) / 16 * 16;
+    p = std::min<int64_t>(p, (int64_t)pkv::kMaxPartitionBlocks * block_size);
+    pre.partition_tokens = (int32_t)p;
+    pre.max_parts = (int32_t)((max_tokens + p - 1) / p);
+  }
+  const int64_t suf_units = (int64_t)n_kv_heads * suf.head_chunks;
+  if (pre_items * pre.max_parts > (int64_t)INT32_MAX ||
+      (int64_t)num_seqs * suf.max_parts * suf_units > (int64_t)INT32_MAX)
+    return fail(PKV_ERR_INVALID, "too many work items");
+
+  // workspace: [split acc | split ml] (shared by the two launches, which run
+  // one after the other) then [prefix acc | prefix ml] per (sequence, head)
+  const size_t split_rows = std::max(pre.max_parts > 1 ? (size_t)pre_items * 16 * pre.max_parts : 0,
+                                     suf.max_parts > 1 ? (size_t)num_seqs * n_heads * suf.max_parts : 0);
+  const size_t pre_rows = (size_t)num_seqs * n_heads;
+  const size_t split_acc = split_rows * head_dim * sizeof(float);
+  const size_t split_ml = split_rows * sizeof(float2);
+  const size_t pre_acc = pre_rows * head_dim * sizeof(float);
+  void *ws = nullptr;
+  int rc = get_workspace(st, split_acc + split_ml + pre_acc + pre_rows * sizeof(float2), &ws);
+  if (rc != PKV_OK) return rc;
+  char *w = static_cast<char *>(ws);
+  if (split_rows) {
+    suf.part_acc = pre.part_acc = reinterpret_cast<float *>(w);
+    suf.part_ml = pre.part_ml = reinterpret_cast<float2 *>(w + split_acc);
+  }
+  suf.pre_acc = pre.pre_acc = reinterpret_cast<float *>(w + split_acc + split_ml);
+  suf.pre_ml = pre.pre_ml = reinterpret_cast<float2 *>(w + split_acc + split_ml + pre_acc);
+  const bool pre_fused = pre.max_parts > 1 && pre.max_parts <= pkv::kFusedMergeParts;
+  const bool suf_fused = suf.max_parts > 1 && suf.max_parts <= pkv::kFusedMergeParts;
+  if (pre_fused || suf_fused) {
+    // one counter set serves both launches: each leaves its counters at zero
+    int32_t *arr = nullptr;
+    rc = get_arrivals(st, std::max(pre_fused ? pre_items : 0, suf_fused ? (int64_t)num_seqs * suf_units : 0), &arr);
+    if (rc != PKV_OK) return rc;
+    if (pre_fused) pre.arrivals = arr;
+    if (suf_fused) suf.arrivals = arr;
+  }
+  hipError_t e = pkv::launch_shared_prefix(static_cast<pkv::DType>(dtype), head_dim, pre, suf, st);
+  if (e != hipSuccess) return hip_fail(e, "shared-prefix decode launch");
   return ok();
 }
 

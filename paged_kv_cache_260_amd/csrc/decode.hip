@@ -73,9 +73,12 @@ template <typename T, int D, int GT> struct Cfg {
   static constexpr int kMlOff = kNW * kWaveBytes;        // workgroup-wide
   static constexpr int kBadOff = kMlOff + kNW * GT * 8;
   static constexpr int kFlagOff = kBadOff + kNW * 4;
+  // shared mode: per member of the item, [0, 16) last-arrival flags, [16, 32)
+  // slot totals, [32, 48) own slot base
+  static constexpr int kMemOff = kFlagOff + 4;
   // Q of the item (its GT head rows, swizzled like a K tile), shared by the
   // four waves as the MFMA A operand; rows GT..15 of the operand are zero
-  static constexpr int kQOff = (kFlagOff + 4 + 15) / 16 * 16;
+  static constexpr int kQOff = (kMemOff + 48 * 4 + 15) / 16 * 16;
   static constexpr int kQChunks = GT * kCh;
   static constexpr int kSmem = kQOff + kQChunks * 16;
   static_assert(kCh % 4 == 0 && 64 % kCh == 0, "head_dim must give 8, 16 or 32 chunks");
@@ -94,6 +97,13 @@ template <typename T, int D, int GT> struct Cfg {
 // ballots over 64-sequence chunks held in registers), so no workgroup-wide
 // synchronisation is needed.
 constexpr int kCompactSeqs = 256;
+
+// What a work item's rows are (decode_item).
+constexpr int kModeDecode = 0;
+constexpr int kModeChunk = 1;
+constexpr int kModePrefix = 2;
+constexpr int kModeSuffix = 3;
+constexpr int kModeShared = 4;
 constexpr int kCompactChunks = kCompactSeqs / 64;
 constexpr int kRemBuckets = 8;
 
@@ -101,6 +111,7 @@ struct ItemPlan {
   int fb[kCompactChunks];  // per lane: (full partitions << 4) | bucket, bucket 15 = no sequence
   int full_items;          // full partitions of the batch (uniform)
   int items;               // all items of one unit (uniform)
+  int p_pre;               // shared mode: partition length of the prefix entities (uniform)
 };
 
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
@@ -112,7 +123,23 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
   return x;
 }
 
-__device__ __forceinline__ void make_plan(const DecodeArgs &a, ItemPlan &pl) {
+// The length that orders an item is the number of tokens it walks: the
+// sequence length (decode, chunk), the group's prefix length (prefix mode) or
+// the tokens after the prefix (suffix mode).
+// Shared mode: prefix partitions are cut about as long as the longest private
+// part (rounded up to whole blocks), never shorter than the host's minimum
+// (which keeps every row's slots within the in-kernel merge) and never longer
+// than kMaxPartitionBlocks blocks. Items then take similar times, and a long
+// prefix is not cut into more items than the private parts already give.
+__device__ __forceinline__ int shared_prefix_partition(const DecodeArgs &a, int max_private) {
+  if (a.prefix_partition_fixed) return a.prefix_partition_tokens;
+  const int bs = a.block_size;
+  int p = (max_private + bs - 1) / bs * bs;
+  p = max(p, a.prefix_partition_tokens);
+  return min(p, kMaxPartitionBlocks * bs);
+}
+
+template <int MODE> __device__ __forceinline__ void make_plan(const DecodeArgs &a, ItemPlan &pl) {
   const int lane = threadIdx.x & 63;
   const int B = a.num_seqs;
   const int P = a.partition_tokens;
@@ -120,18 +147,67 @@ __device__ __forceinline__ void make_plan(const DecodeArgs &a, ItemPlan &pl) {
   // all chunk loads first (clamped index, no branches), so they are in flight
   // together and one wait covers them
   int Ls[kCompactChunks];
+  int Pe[kCompactChunks];  // partition length of each lane's entity
 #pragma unroll
-  for (int c = 0; c < kCompactChunks; ++c) Ls[c] = a.seq_lens[min(c * 64 + lane, B - 1)];
+  for (int c = 0; c < kCompactChunks; ++c) Pe[c] = P;
+  if constexpr (MODE == kModeShared) {
+    // entities: the groups' prefixes, then the sequences' private tokens
+    const int ng = a.num_groups;
+    int first[kCompactChunks], len[kCompactChunks], pre[kCompactChunks];
+#pragma unroll
+    for (int c = 0; c < kCompactChunks; ++c) {
+      const int e = min(c * 64 + lane, B - 1);
+      first[c] = e < ng ? a.query_start_loc[e] : e - ng;
+    }
+#pragma unroll
+    for (int c = 0; c < kCompactChunks; ++c) {
+      const int m = min(max(first[c], 0), a.member_seqs - 1);
+      len[c] = a.seq_lens[m];
+      pre[c] = a.prefix_lens[m];
+    }
+    int max_private = 0;
+#pragma unroll
+    for (int c = 0; c < kCompactChunks; ++c) {
+      const bool is_pre = c * 64 + lane < ng;
+      Ls[c] = is_pre ? pre[c] : (pre[c] >= 0 && pre[c] <= len[c] ? len[c] - pre[c] : -1);
+      if (!is_pre && c * 64 + lane < B && (int64_t)len[c] <= max_tok) max_private = max(max_private, Ls[c]);
+    }
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) max_private = max(max_private, __shfl_xor(max_private, d, 64));
+    pl.p_pre = __builtin_amdgcn_readfirstlane(shared_prefix_partition(a, max_private));
+#pragma unroll
+    for (int c = 0; c < kCompactChunks; ++c) Pe[c] = c * 64 + lane < ng ? pl.p_pre : P;
+  } else if constexpr (MODE == kModePrefix) {
+    int first[kCompactChunks];
+#pragma unroll
+    for (int c = 0; c < kCompactChunks; ++c) first[c] = a.query_start_loc[min(c * 64 + lane, B - 1)];
+#pragma unroll
+    for (int c = 0; c < kCompactChunks; ++c)
+      Ls[c] = a.prefix_lens[min(max(first[c], 0), a.member_seqs - 1)];
+  } else if constexpr (MODE == kModeSuffix) {
+    int pre[kCompactChunks];
+#pragma unroll
+    for (int c = 0; c < kCompactChunks; ++c) {
+      Ls[c] = a.seq_lens[min(c * 64 + lane, B - 1)];
+      pre[c] = a.prefix_lens[min(c * 64 + lane, B - 1)];
+    }
+#pragma unroll
+    for (int c = 0; c < kCompactChunks; ++c) Ls[c] = pre[c] >= 0 && pre[c] <= Ls[c] ? Ls[c] - pre[c] : -1;
+  } else {
+#pragma unroll
+    for (int c = 0; c < kCompactChunks; ++c) Ls[c] = a.seq_lens[min(c * 64 + lane, B - 1)];
+  }
   int full_sum = 0;
 #pragma unroll
   for (int c = 0; c < kCompactChunks; ++c) {
     pl.fb[c] = 15;
     if (c * 64 + lane < B) {
       const int L = Ls[c];
+      const int Pc = Pe[c];
       const bool ok = L > 0 && (int64_t)L <= max_tok;
-      const int full = ok ? (L - 1) / P : 0;
-      const int rem = L - full * P;  // 1 .. P when ok
-      pl.fb[c] = (full << 4) | (ok ? (int)(((int64_t)(P - rem) * kRemBuckets) / P) : kRemBuckets);
+      const int full = ok ? (L - 1) / Pc : 0;
+      const int rem = L - full * Pc;  // 1 .. Pc when ok
+      pl.fb[c] = (full << 4) | (ok ? (int)(((int64_t)(Pc - rem) * kRemBuckets) / Pc) : kRemBuckets);
       full_sum += full;
     }
   }
@@ -189,22 +265,58 @@ __device__ __forceinline__ void locate_item(const ItemPlan &pl, int B, int j, in
   p_out = p_res;
 }
 
+// Output value of a row from its own un-normalised state (M, num, den) and a
+// second partial (pm = (m, l), pa = acc) of the same row:
+//   (2^(M - M') num + 2^(m - M') pa) / (2^(M - M') den + 2^(m - M') l),
+// M' = max(M, m); a state with max -inf contributes nothing; NaN propagates.
+__device__ __forceinline__ float fold_partial(float M, float num, float den, float2 pm, float pa) {
+  const float Mt = fmaxf(M, pm.x);
+  const float f = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mt);
+  const float fp = pm.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(pm.x - Mt);
+  if (M != M || pm.x != pm.x) return __builtin_nanf("");
+  return fmaf(f, num, fp * pa) / fmaf(f, den, fp * pm.y);
+}
+
 // One work item: query heads [hc GT, hc GT + GT) of KV head g (unit = g x
 // head chunk hc) over tokens [part P, part P + P) of sequence s.
 // F8: the pools hold OCP e4m3 codes with one scale per KV head (k_scale,
 // v_scale); tiles are decoded to T on their way into LDS, k_scale is folded
 // into the score scale and v_scale into the output (partials included).
-// CH (chunk rows, GT = 16): the sequence's last n = qsl[s+1] - qsl[s] tokens
-// are queries, and the item's 16 rows are (chunk token, query head of g)
-// pairs, token-major from row 16 hc (unit = g x row block hc): row r is
-// token r / G, head g G + r % G. Chunk token i sits at position L - n + i and
-// sees tokens 0 .. L - n + i only, so each row carries its own last visible
-// token; the item's context ends after its last row's position.
-template <typename T, int D, int GT, bool F8, bool CH>
-__device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int tid, int unit, int s, int part) {
+// MODE selects what the item's rows are:
+//   kModeDecode: query heads of sequence s, as above.
+//   kModeChunk (GT = 16): the sequence's last n = qsl[s+1] - qsl[s] tokens are
+//     queries, and the item's 16 rows are (chunk token, query head of g)
+//     pairs, token-major from row 16 hc (unit = g x row block hc): row r is
+//     token r / G, head g G + r % G. Chunk token i sits at position L - n + i
+//     and sees tokens 0 .. L - n + i only, so each row carries its own last
+//     visible token; the item's context ends after its last row's position.
+//   kModePrefix (GT = 16): s is a group of sequences qsl[s] .. qsl[s+1] - 1
+//     that share their first prefix_lens[qsl[s]] tokens (the same physical
+//     blocks); rows are (member, query head of g) pairs laid out as in chunk
+//     mode, all seeing the whole prefix, read once through the first member's
+//     table. Results are un-normalised partials (pre_acc, pre_ml) per
+//     (sequence, head) row, not outputs.
+//   kModeSuffix: decode of sequence s over tokens [prefix_lens[s], L) only;
+//     the row that finishes a (sequence, head) output folds in its prefix
+//     partial (when prefix_lens[s] > 0).
+//   kModeShared (GT = 16, one launch for both): entity s < num_groups is the
+//     prefix of group s (as in kModePrefix, all members in one 16-row block,
+//     partitions of prefix_partition_tokens); entity num_groups + i is the
+//     private tokens of sequence i (rows: its G heads). Every partition of
+//     either kind stores its rows' partial state in a slot of the (sequence,
+//     head) row: prefix partition p in slot p, private partition p in slot
+//     ceil(prefix / prefix partition) + p. The last partition to finish for a
+//     (sequence, KV head) merges all of that row set's slots.
+template <typename T, int D, int GT, bool F8, int MODE>
+__device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int tid, int unit, int s, int part,
+                                            int p_pre) {
   using C = Cfg<T, D, GT>;
+  // rows mode: item rows are (token or member, head) pairs
+  constexpr bool RM = MODE == kModeChunk || MODE == kModePrefix || MODE == kModeShared;
+  constexpr bool SH = MODE == kModeShared;
   static_assert(!F8 || C::kPvMfma, "FP8 pools need a 16-bit query type");
-  static_assert(!CH || (GT == 16 && C::kPvMfma), "chunk rows: 16-row tiles, 16-bit types");
+  static_assert(!RM || (GT == 16 && C::kPvMfma), "chunk rows: 16-row tiles, 16-bit types");
+  static_assert(MODE != kModeSuffix || C::kPvMfma, "shared-prefix decode: 16-bit types");
   constexpr int kKvBytes = F8 ? 1 : (int)sizeof(T);     // bytes per stored element
   constexpr int kL = kTileTokens * D * kKvBytes / (16 * 64);  // 16-byte loads per lane per K (or V) tile
   constexpr int kChKV = D * kKvBytes / 16;               // 16-byte chunks per stored token row
@@ -223,14 +335,29 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   // chunk rows: first query token of the sequence, chunk length, first row
   int q0 = 0, nq = 0;
   const int row0 = hc * GT;
-  if constexpr (CH) {
+  // rows mode with a bad range (a caller error): the item has no rows and
+  // touches nothing
+  bool bad_rows = false;
+  // shared mode: a prefix entity (else the private tokens of sequence q0)
+  const bool pre_item = SH && s < a.num_groups;
+  if constexpr (SH) {
+    if (pre_item) {
+      q0 = a.query_start_loc[s];
+      nq = a.query_start_loc[s + 1] - q0;
+    } else {
+      q0 = s - a.num_groups;
+      nq = 1;
+    }
+    bad_rows = q0 < 0 || nq < 1 || q0 + nq > a.member_seqs;
+  } else if constexpr (RM) {
     q0 = a.query_start_loc[s];
     nq = a.query_start_loc[s + 1] - q0;
+    bad_rows = q0 < 0 || (MODE == kModePrefix && (nq < 1 || q0 + nq > a.member_seqs));
   }
-  const int nh = CH ? max(0, min(GT, nq * G - row0)) : min(GT, G - hc * GT);
+  const int nh = RM ? (bad_rows ? 0 : max(0, min(GT, nq * G - row0))) : min(GT, G - hc * GT);
   // output (and query) row of item row i
   auto row_index = [&](int i) -> int64_t {
-    if constexpr (CH) {
+    if constexpr (RM) {
       const int r = row0 + i;
       return (int64_t)(q0 + r / G) * H + g * G + r % G;
     } else {
@@ -239,7 +366,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   };
   // partial-result row of item row i (split items)
   auto part_row = [&](int i) -> int64_t {
-    if constexpr (CH) return ((int64_t)s * units + unit) * GT + i;
+    if constexpr (SH) return row_index(i);
+    else if constexpr (RM) return ((int64_t)s * units + unit) * GT + i;
     else return (int64_t)s * H + head0 + i;
   };
   float sl2 = a.scale_log2;  // scores in base-2 units
@@ -249,21 +377,27 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
     vsc = a.v_scale[g];
   }
 
-  const int P = a.partition_tokens;
-  const int start = part * P;
+  const int P = pre_item ? p_pre : a.partition_tokens;
+  // suffix mode (and private entities): the tokens start after the shared prefix
+  int tok0 = 0;
+  if constexpr (MODE == kModeSuffix) tok0 = a.prefix_lens[s];
+  if constexpr (SH) tok0 = pre_item || bad_rows ? 0 : a.prefix_lens[q0];
+  const int start = max(tok0, 0) + part * P;
   const int kg = lane >> 4;
   const int n = lane & 15;
   // Issue the length, the partition's table entries and q together; none of
   // these addresses depends on the length. Table entries past the sequence
-  // (but inside the row) are read and ignored.
-  const int32_t *bt_row = a.block_tables + (int64_t)s * a.max_blocks;
+  // (but inside the row) are read and ignored. Prefix mode reads the table
+  // of the group's first member.
+  const int32_t *bt_row =
+      a.block_tables + (int64_t)(MODE == kModePrefix || SH ? (bad_rows ? 0 : q0) : s) * a.max_blocks;
   const int jb = start >> a.block_shift;
   const int btv_raw = jb + lane < a.max_blocks ? bt_row[jb + lane] : 0;
   // Q chunks of this thread: chunk u = tid + 256 i of the GT x kCh head-row
   // block (rows past nh are zero)
   constexpr int kQPer = (C::kQChunks + kNW * 64 - 1) / (kNW * 64);
   u32x4_t qv[kQPer];
-  if constexpr (CH) {
+  if constexpr (RM) {
 #pragma unroll
     for (int i = 0; i < kQPer; ++i) {
       const int u = tid + i * kNW * 64;
@@ -281,29 +415,106 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
       if (u < C::kQChunks && u / kCh < nh) qv[i] = qblk[u];
     }
   }
-  const int L = a.seq_lens[s];
-  if (CH && nh == 0) return;  // no query rows (empty chunk, or past its last row)
-  const bool bad_len = L < 0 || (int64_t)L > (int64_t)a.max_blocks * a.block_size || (CH && (L < nq || q0 < 0));
-  if (bad_len || L == 0) {
-    if (part == 0) {
-      const float v = bad_len ? __builtin_nanf("") : 0.f;
-      for (int i = tid; i < nh * D; i += kNW * 64)
-        out[row_index(i / D) * D + i % D] = static_cast<T>(v);
+  // no query rows: empty chunk, past its last row, or a bad range
+  if (RM && nh == 0) return;
+  // shared mode: members of the item (whole members only: G divides 16), and
+  // for a prefix item each member's length and prefix (thread t < nmem)
+  const int nmem = SH ? (pre_item ? nh / G : 1) : 0;
+  int mem_len = 0, mem_pre = 0;
+  if constexpr (SH) {
+    if (pre_item && tid < nmem) {
+      mem_len = a.seq_lens[q0 + tid];
+      mem_pre = a.prefix_lens[q0 + tid];
     }
-    return;
   }
-  // tokens the item's rows may see: [0, ctx)
-  const int ctx = CH ? L - nq + (row0 + nh - 1) / G + 1 : L;
+  // Prefix mode: a prefix that is empty or not a whole number of blocks is
+  // left to the suffix launch (nothing to fold, or NaN rows).
+  const int L = MODE == kModePrefix || pre_item ? a.prefix_lens[q0] : (SH ? a.seq_lens[q0] : a.seq_lens[s]);
+  const int64_t cap = (int64_t)a.max_blocks * a.block_size;
+  bool bad_len = L < 0 || (int64_t)L > cap;
+  if constexpr (MODE == kModeChunk) bad_len |= L < nq || q0 < 0;
+  if constexpr (MODE == kModePrefix) bad_len |= (L & (a.block_size - 1)) != 0;
+  if constexpr (MODE == kModeSuffix) bad_len |= tok0 < 0 || tok0 > L || (tok0 & (a.block_size - 1)) != 0;
+  if constexpr (SH) {
+    if (pre_item) bad_len |= (L & (a.block_size - 1)) != 0;
+    else bad_len |= tok0 < 0 || tok0 > L || (tok0 & (a.block_size - 1)) != 0;
+  }
+  if constexpr (MODE == kModePrefix) {
+    if (bad_len || L == 0) return;
+  } else if constexpr (SH) {
+    // a prefix entity that is invalid or empty does nothing (its members'
+    // private entities see the same prefix value: NaN rows, or no prefix);
+    // a private entity that is invalid writes NaN rows; one with no private
+    // token leaves its rows to the prefix partitions (zeros when empty)
+    if (pre_item) {
+      if (bad_len || L == 0) return;
+    } else if (bad_len || L == tok0) {
+      if (part == 0 && (bad_len || L == 0)) {
+        const float v = bad_len ? __builtin_nanf("") : 0.f;
+        for (int i = tid; i < nh * D; i += kNW * 64)
+          out[row_index(i / D) * D + i % D] = static_cast<T>(v);
+      }
+      return;
+    }
+  } else if constexpr (MODE == kModeSuffix) {
+    if (bad_len || L == tok0) {
+      // invalid, or nothing after the prefix: the output is the prefix result
+      // alone (zeros for an empty sequence)
+      if (part == 0) {
+        for (int i = tid; i < nh * D; i += kNW * 64) {
+          const int64_t row = row_index(i / D);
+          float v = bad_len ? __builtin_nanf("") : 0.f;
+          if (!bad_len && tok0 > 0) {
+            const float2 pm = a.pre_ml[row];
+            v = a.pre_acc[row * D + i % D] / pm.y;
+          }
+          out[row * D + i % D] = static_cast<T>(v);
+        }
+      }
+      return;
+    }
+  } else {
+    if (bad_len || L == 0) {
+      if (part == 0) {
+        const float v = bad_len ? __builtin_nanf("") : 0.f;
+        for (int i = tid; i < nh * D; i += kNW * 64)
+          out[row_index(i / D) * D + i % D] = static_cast<T>(v);
+      }
+      return;
+    }
+  }
+  // tokens the item's rows may see: [tok0, ctx)
+  const int ctx = MODE == kModeChunk ? L - nq + (row0 + nh - 1) / G + 1 : L;
   // last visible token of rows 4 kg + r of this lane (chunk rows)
   int lim[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int i = 4 * (lane >> 4) + r;
-    lim[r] = CH && i < nh ? L - nq + (row0 + i) / G : (CH ? -1 : INT32_MAX);
+    lim[r] = i < nh ? L - nq + (row0 + i) / G : -1;
   }
   if (start >= ctx) return;
   const int end = min(ctx, start + P);
-  const int nparts = (ctx + P - 1) / P;
+  const int nparts = (ctx - tok0 + P - 1) / P;
+  // shared mode: slot of this partition, and slot totals per member
+  //   prefix partitions of a member: ceil(prefix / prefix partition)
+  //   private partitions: ceil((L - prefix) / partition)
+  const int npre_own = SH && !pre_item && tok0 > 0 ? (tok0 + p_pre - 1) / p_pre : 0;
+  const int sbase = npre_own;  // prefix partitions come first
+  int mem_tot = 0;             // thread t < nmem: slots of member t (0: not counted by this item)
+  if constexpr (SH) {
+    if (pre_item) {
+      const bool ok = mem_pre == L && mem_len >= mem_pre && (int64_t)mem_len <= cap;
+      mem_tot = ok ? nparts + (mem_len - mem_pre + a.partition_tokens - 1) / a.partition_tokens : 0;
+    } else {
+      mem_tot = npre_own + nparts;
+    }
+  }
+  // Folds the prefix partial of output row `row` (dimension d) into this
+  // row's own (M, num, den) and returns the output value (suffix mode).
+  auto fold_prefix = [&](int64_t row, int d, float M, float num, float den) -> float {
+    if (MODE != kModeSuffix || tok0 == 0) return num / den;
+    return fold_partial(M, num, den, a.pre_ml[row], a.pre_acc[row * D + d]);
+  };
 
   // Block ids of the partition (at most 64 table entries): lane i of btv holds
   // entry jb + i. They are read back with v_readlane, so the per-tile lookup
@@ -460,7 +671,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
     bool over = false;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      if constexpr (CH)
+      if constexpr (MODE == kModeChunk)
         z[r] = tok_ok && ti * kTileTokens + n <= lim[r] ? sc[r] * sl2 : -INFINITY;
       else
         z[r] = tok_ok ? sc[r] * sl2 : -INFINITY;
@@ -473,7 +684,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
         const float mn = fmaxf(m[r], row_max16(z[r]));
         alpha[r] = __builtin_amdgcn_exp2f(m[r] - mn);  // 0 on the first tile (m = -inf)
         // chunk rows may have seen nothing yet (mn = -inf): keep them empty
-        if constexpr (CH) alpha[r] = mn == -INFINITY ? 1.f : alpha[r];
+        if constexpr (MODE == kModeChunk) alpha[r] = mn == -INFINITY ? 1.f : alpha[r];
         m[r] = mn;
         l[r] *= alpha[r];
       }
@@ -495,7 +706,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       p[r] = __builtin_amdgcn_exp2f(z[r] - m[r]);
-      if constexpr (CH) p[r] = z[r] == -INFINITY ? 0.f : p[r];  // also when m = -inf
+      if constexpr (MODE == kModeChunk) p[r] = z[r] == -INFINITY ? 0.f : p[r];  // also when m = -inf
       l[r] += p[r];
     }
 
@@ -572,6 +783,11 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
     if (u < C::kQChunks)
       reinterpret_cast<u32x4_t *>(smem + C::kQOff)[kst_slot<kCh>(u / kCh, u % kCh)] = qv[i];
   }
+  int *mflag = reinterpret_cast<int *>(smem + C::kMemOff);  // shared mode: [16] flags
+  int *mtot = mflag + 16;                                     // [16] slot totals per member
+  if constexpr (SH) {
+    if (tid < 16) mtot[tid] = tid < nmem ? mem_tot : 0;
+  }
   __syncthreads();
   if constexpr (C::kPvMfma) {
     for (int ti = tb + wave; ti < te; ti += kNW) process(ti, rg, ti + kNW < te ? ti + kNW : -1);
@@ -632,7 +848,13 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   int any_bad = 0;
 #pragma unroll
   for (int w = 0; w < kNW; ++w) any_bad |= mbad[w];
-  const bool fused = nparts > 1 && a.arrivals != nullptr;
+  // shared mode: every split row is merged in the kernel (at most
+  // kFusedMergeParts slots); skip the arrival step when no member is split
+  bool any_split = false;
+  if constexpr (SH) {
+    for (int t = 0; t < nmem; ++t) any_split |= mtot[t] > 1;
+  }
+  const bool fused = SH ? any_split : (nparts > 1 && a.arrivals != nullptr);
   float rM[kPer], rnum[kPer], rden[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
@@ -660,10 +882,20 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
     rM[k] = M;
     rnum[k] = num;
     rden[k] = den;
-    if (nparts == 1) {
-      out[row_index(h) * D + d] = static_cast<T>(num / den);
+    // slots of this row's (sequence, head) and this partition's own slot
+    const int tot = SH ? mtot[h / G] : nparts;
+    const int own = SH ? sbase + part : part;
+    if (SH && tot == 0) continue;  // member not counted here (invalid)
+    if (tot == 1) {
+      if constexpr (MODE == kModePrefix) {
+        const int64_t row = row_index(h);
+        a.pre_acc[row * D + d] = num;
+        if (d == 0) a.pre_ml[row] = make_float2(M, den);
+      } else {
+        out[row_index(h) * D + d] = static_cast<T>(fold_prefix(row_index(h), d, M, num, den));
+      }
     } else {
-      const int64_t pi = part_row(h) * a.max_parts + part;
+      const int64_t pi = part_row(h) * a.max_parts + own;
       if (!fused) {
         a.part_acc[pi * D + d] = num;
         if (d == 0) a.part_ml[pi] = make_float2(M, den);
@@ -690,14 +922,34 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   int *flag = reinterpret_cast<int *>(smem + C::kFlagOff);
-  if (tid == 0) {
+  if constexpr (SH) {
+    // one counter per (member sequence, KV head); each split member counts
+    // this partition once
+    int any_last = 0;
+    if (tid < nmem) {
+      const int t = mtot[tid];
+      int last = 0;
+      if (t > 1) {
+        int32_t *cnt = a.arrivals + (int64_t)(q0 + tid) * a.n_kv_heads + g;
+        const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = prev == t - 1;
+        if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      mflag[tid] = last;
+      any_last = last;
+    }
+    if (tid == 0) *flag = 0;
+    __syncthreads();
+    if (any_last) *flag = 1;  // benign race: every writer stores 1
+    __syncthreads();
+  } else if (tid == 0) {
     int32_t *cnt = a.arrivals + (int64_t)s * units + unit;
     const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int last = prev == nparts - 1;
     if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *flag = last;
   }
-  __syncthreads();
+  if constexpr (!SH) __syncthreads();
   if (!*flag) return;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
@@ -706,13 +958,16 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
     const int h = idx / D;
     const int d = idx - h * D;
     const int64_t prow = part_row(h);
+    if (SH && !mflag[h / G]) continue;  // this member is merged by another partition
+    const int tot = SH ? mtot[h / G] : nparts;
+    const int own = SH ? sbase + part : part;
     float2 oml[kFusedMergeParts];
     float ox[kFusedMergeParts];
 #pragma unroll
     for (int p = 0; p < kFusedMergeParts; ++p) {
       oml[p] = make_float2(-INFINITY, 0.f);
       ox[p] = 0.f;
-      if (p < nparts && p != part) {
+      if (p < tot && p != own) {
         const int64_t pi = prow * a.max_parts + p;
         oml[p] = __builtin_bit_cast(
             float2, __hip_atomic_load(reinterpret_cast<unsigned long long *>(a.part_ml + pi),
@@ -735,7 +990,14 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
       den = fmaf(f, oml[p].y, den);
       num = fmaf(f, ox[p], num);
     }
-    out[row_index(h) * D + d] = static_cast<T>(bad ? __builtin_nanf("") : num / den);
+    if constexpr (MODE == kModePrefix) {
+      const int64_t row = row_index(h);
+      a.pre_acc[row * D + d] = bad ? __builtin_nanf("") : num;
+      if (d == 0) a.pre_ml[row] = make_float2(bad ? __builtin_nanf("") : M, den);
+    } else {
+      if (bad) M = num = den = __builtin_nanf("");
+      out[row_index(h) * D + d] = static_cast<T>(fold_prefix(row_index(h), d, M, num, den));
+    }
   }
 }
 
@@ -746,7 +1008,7 @@ template <typename T, int D, int GT> constexpr int decode_waves_per_eu() {
   return (sizeof(T) == 2 || GT <= 4) ? 3 : 2;
 }
 
-template <typename T, int D, int GT, bool F8, bool CH>
+template <typename T, int D, int GT, bool F8, int MODE>
 __global__ __launch_bounds__(kDecodeWaves * 64)
 __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT>()))) void paged_decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[Cfg<T, D, GT>::kSmem];
@@ -768,7 +1030,8 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT>()))) void paged
   const int w = (int)(lin / units);
   const bool compact = a.num_seqs <= kCompactSeqs;
   ItemPlan plan;
-  if (compact) make_plan(a, plan);
+  plan.p_pre = a.prefix_partition_tokens;
+  if (compact) make_plan<MODE>(a, plan);
   for (int round = 0;; ++round) {
     int s, part;
     if (compact) {
@@ -789,7 +1052,8 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT>()))) void paged
     // held in registers through the tile loop.
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    decode_item<T, D, GT, F8, CH>(a, smem, tid, unit, s, part);
+    // prefix partition length (shared mode): the plan's, or the host's minimum
+    decode_item<T, D, GT, F8, MODE>(a, smem, tid, unit, s, part, compact ? plan.p_pre : a.prefix_partition_tokens);
   }
 }
 
@@ -812,8 +1076,12 @@ __global__ __launch_bounds__(kReduceThreads) void paged_decode_reduce_kernel(Dec
   const int s = blockIdx.y;
   const int L = a.seq_lens[s];
   const int P = a.partition_tokens;
-  if (L <= P || (int64_t)L > (int64_t)a.max_blocks * a.block_size) return;  // single partition or invalid
-  const int nparts = (L + P - 1) / P;
+  // suffix mode (shared-prefix decode): partitions start after the prefix
+  const int tok0 = a.prefix_lens ? a.prefix_lens[s] : 0;
+  if (tok0 < 0 || (tok0 & (a.block_size - 1)) != 0 || L - tok0 <= P ||
+      (int64_t)L > (int64_t)a.max_blocks * a.block_size)
+    return;  // single partition or invalid
+  const int nparts = (L - tok0 + P - 1) / P;
   const int d = threadIdx.x % D;
   const int grp = threadIdx.x / D;
   const int64_t row = (int64_t)s * a.n_heads + h;
@@ -879,7 +1147,9 @@ __global__ __launch_bounds__(kReduceThreads) void paged_decode_reduce_kernel(Dec
       dt = fmaf(f, v.y, dt);
       nt = fmaf(f, red_num[g2][d], nt);
     }
-    static_cast<T *>(a.out)[row * D + d] = static_cast<T>(any_bad ? __builtin_nanf("") : nt / dt);
+    float o = any_bad ? __builtin_nanf("") : nt / dt;
+    if (tok0 > 0 && !any_bad) o = fold_partial(Mt, nt, dt, a.pre_ml[row], a.pre_acc[row * D + d]);
+    static_cast<T *>(a.out)[row * D + d] = static_cast<T>(o);
   }
 }
 
@@ -907,8 +1177,11 @@ __global__ __launch_bounds__(kMergeThreads) void paged_decode_merge_few_kernel(D
   const int hb = blockIdx.x - s * hblocks;
   const int L = a.seq_lens[s];
   const int P = a.partition_tokens;
-  if (L <= P || (int64_t)L > (int64_t)a.max_blocks * a.block_size) return;  // single partition or invalid
-  const int nparts = (L + P - 1) / P;  // 2 .. max_parts <= kFewParts
+  const int tok0 = a.prefix_lens ? a.prefix_lens[s] : 0;  // suffix mode
+  if (tok0 < 0 || (tok0 & (a.block_size - 1)) != 0 || L - tok0 <= P ||
+      (int64_t)L > (int64_t)a.max_blocks * a.block_size)
+    return;  // single partition or invalid
+  const int nparts = (L - tok0 + P - 1) / P;  // 2 .. max_parts <= kFewParts
   const int d = threadIdx.x % D;
   const int hl = threadIdx.x / D;
   float2 ml[kHPT][kFewParts];
@@ -946,8 +1219,10 @@ __global__ __launch_bounds__(kMergeThreads) void paged_decode_merge_few_kernel(D
       den = fmaf(f, ml[j][p].y, den);
       num = fmaf(f, x[j][p], num);
     }
-    static_cast<T *>(a.out)[((int64_t)s * a.n_heads + h) * D + d] =
-        static_cast<T>(bad ? __builtin_nanf("") : num / den);
+    const int64_t row = (int64_t)s * a.n_heads + h;
+    float o = bad ? __builtin_nanf("") : num / den;
+    if (tok0 > 0 && !bad) o = fold_partial(M, num, den, a.pre_ml[row], a.pre_acc[row * D + d]);
+    static_cast<T *>(a.out)[row * D + d] = static_cast<T>(o);
   }
 }
 
@@ -958,8 +1233,9 @@ __global__ __launch_bounds__(kMergeThreads) void paged_decode_merge_few_kernel(D
 // m = -inf and are skipped).
 constexpr int kChunkReduceThreads = 256;
 
-template <typename T, int D>
+template <typename T, int D, int MODE>
 __global__ __launch_bounds__(kChunkReduceThreads) void paged_chunk_reduce_kernel(DecodeArgs a) {
+  static_assert(MODE == kModeChunk || MODE == kModePrefix, "rows modes");
   constexpr int kRows = 16;
   const int units = a.n_kv_heads * a.head_chunks;
   const int s = (int)(blockIdx.x / (unsigned)units);
@@ -969,10 +1245,13 @@ __global__ __launch_bounds__(kChunkReduceThreads) void paged_chunk_reduce_kernel
   const int G = a.group;
   const int q0 = a.query_start_loc[s];
   const int nq = a.query_start_loc[s + 1] - q0;
-  const int L = a.seq_lens[s];
+  if (q0 < 0 || (MODE == kModePrefix && (nq < 1 || q0 + nq > a.member_seqs))) return;
+  const int L = MODE == kModePrefix ? a.prefix_lens[q0] : a.seq_lens[s];
   const int nh = max(0, min(kRows, nq * G - row0));
-  if (nh == 0 || L < nq || q0 < 0 || (int64_t)L > (int64_t)a.max_blocks * a.block_size) return;
-  const int ctx = L - nq + (row0 + nh - 1) / G + 1;
+  if (nh == 0 || (int64_t)L > (int64_t)a.max_blocks * a.block_size) return;
+  if (MODE == kModeChunk && L < nq) return;
+  if (MODE == kModePrefix && (L <= 0 || (L & (a.block_size - 1)) != 0)) return;
+  const int ctx = MODE == kModeChunk ? L - nq + (row0 + nh - 1) / G + 1 : L;
   const int P = a.partition_tokens;
   const int nparts = (ctx + P - 1) / P;
   if (nparts <= 1) return;  // written by the attention kernel
@@ -997,10 +1276,17 @@ __global__ __launch_bounds__(kChunkReduceThreads) void paged_chunk_reduce_kernel
       M = mn;
     }
     const int r = row0 + i;
-    static_cast<T *>(a.out)[((int64_t)(q0 + r / G) * a.n_heads + g * G + r % G) * D + d] =
-        static_cast<T>(bad ? __builtin_nanf("") : num / den);
+    const int64_t orow = (int64_t)(q0 + r / G) * a.n_heads + g * G + r % G;
+    if constexpr (MODE == kModePrefix) {
+      a.pre_acc[orow * D + d] = bad ? __builtin_nanf("") : num;
+      if (d == 0) a.pre_ml[orow] = make_float2(bad ? __builtin_nanf("") : M, den);
+    } else {
+      static_cast<T *>(a.out)[orow * D + d] = static_cast<T>(bad ? __builtin_nanf("") : num / den);
+    }
   }
 }
+
+}  // namespace
 
 // Compute units of the current device (cached per device).
 int device_cus() {
@@ -1014,12 +1300,14 @@ int device_cus() {
   return n;
 }
 
+namespace {
+
 // Decode workgroups per unit in the longest-first mode: at least one per
 // sequence and enough for kWgsPerSlot rounds of the chip's resident slots,
 // never more than the unit's largest possible item count.
 constexpr int kWgsPerSlot = 2;
 
-template <typename T, int D, int GT, bool F8, bool CH = false>
+template <typename T, int D, int GT, bool F8, int MODE = kModeDecode>
 hipError_t launch_t(const DecodeArgs &args, hipStream_t stream) {
   DecodeArgs a = args;
   const int64_t units = (int64_t)a.n_kv_heads * a.head_chunks;
@@ -1027,7 +1315,7 @@ hipError_t launch_t(const DecodeArgs &args, hipStream_t stream) {
   if (a.num_seqs <= kCompactSeqs) {
     static const int per_cu = [] {
       int nb = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, paged_decode_kernel<T, D, GT, F8, CH>, kDecodeWaves * 64, 0) !=
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, paged_decode_kernel<T, D, GT, F8, MODE>, kDecodeWaves * 64, 0) !=
               hipSuccess || nb <= 0)
         nb = 1;
       return nb;
@@ -1040,11 +1328,11 @@ hipError_t launch_t(const DecodeArgs &args, hipStream_t stream) {
     a.wgs_per_unit = (int32_t)max_items;
   }
   dim3 grid((unsigned)(units * a.wgs_per_unit), 1, 1);
-  hipLaunchKernelGGL((paged_decode_kernel<T, D, GT, F8, CH>), grid, dim3(kDecodeWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL((paged_decode_kernel<T, D, GT, F8, MODE>), grid, dim3(kDecodeWaves * 64), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.max_parts == 1 || a.arrivals != nullptr) return err;
-  if constexpr (CH) {
-    hipLaunchKernelGGL((paged_chunk_reduce_kernel<T, D>), dim3((unsigned)(units * a.num_seqs)),
+  if constexpr (MODE == kModeChunk || MODE == kModePrefix) {
+    hipLaunchKernelGGL((paged_chunk_reduce_kernel<T, D, MODE>), dim3((unsigned)(units * a.num_seqs)),
                        dim3(kChunkReduceThreads), 0, stream, a);
     return hipGetLastError();
   }
@@ -1062,8 +1350,8 @@ hipError_t launch_t(const DecodeArgs &args, hipStream_t stream) {
 template <typename T, bool F8>
 hipError_t launch_rows_t(int head_dim, const DecodeArgs &a, hipStream_t stream) {
   switch (head_dim) {
-    case 64: return launch_t<T, 64, 16, F8, true>(a, stream);
-    case 128: return launch_t<T, 128, 16, F8, true>(a, stream);
+    case 64: return launch_t<T, 64, 16, F8, kModeChunk>(a, stream);
+    case 128: return launch_t<T, 128, 16, F8, kModeChunk>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1126,6 +1414,57 @@ hipError_t launch_chunk_rows(DType dt, int head_dim, bool fp8, const DecodeArgs 
                                 : launch_rows_t<_Float16, false>(head_dim, a, stream);
     case DType::BF16: return fp8 ? launch_rows_t<__bf16, true>(head_dim, a, stream)
                                  : launch_rows_t<__bf16, false>(head_dim, a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_shared_prefix_td(int gt, const DecodeArgs &pre, const DecodeArgs &suf, hipStream_t stream) {
+  hipError_t e = launch_t<T, D, 16, false, kModePrefix>(pre, stream);
+  if (e != hipSuccess) return e;
+  switch (gt) {
+    case 1: return launch_t<T, D, 1, false, kModeSuffix>(suf, stream);
+    case 2: return launch_t<T, D, 2, false, kModeSuffix>(suf, stream);
+    case 4: return launch_t<T, D, 4, false, kModeSuffix>(suf, stream);
+    case 8: return launch_t<T, D, 8, false, kModeSuffix>(suf, stream);
+    case 16: return launch_t<T, D, 16, false, kModeSuffix>(suf, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+hipError_t launch_shared_fused_t(int head_dim, const DecodeArgs &a, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_t<T, 64, 16, false, kModeShared>(a, stream);
+    case 128: return launch_t<T, 128, 16, false, kModeShared>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+hipError_t launch_shared_prefix_t(int head_dim, int gt, const DecodeArgs &pre, const DecodeArgs &suf,
+                                  hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_shared_prefix_td<T, 64>(gt, pre, suf, stream);
+    case 128: return launch_shared_prefix_td<T, 128>(gt, pre, suf, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_shared_prefix(DType dt, int head_dim, const DecodeArgs &pre, const DecodeArgs &suf,
+                                hipStream_t stream) {
+  const int gt = decode_head_tile(suf.group);
+  switch (dt) {
+    case DType::F16: return launch_shared_prefix_t<_Float16>(head_dim, gt, pre, suf, stream);
+    case DType::BF16: return launch_shared_prefix_t<__bf16>(head_dim, gt, pre, suf, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_shared_fused(DType dt, int head_dim, const DecodeArgs &a, hipStream_t stream) {
+  switch (dt) {
+    case DType::F16: return launch_shared_fused_t<_Float16>(head_dim, a, stream);
+    case DType::BF16: return launch_shared_fused_t<__bf16>(head_dim, a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -50,12 +50,36 @@ struct DecodeArgs {
   // Chunk rows only (launch_chunk_rows): [num_seqs + 1] offsets of each
   // sequence's query tokens; head_chunks then counts 16-row blocks per KV head
   // and partial rows are indexed per item: ((s * units + unit) * 16 + row).
+  // Prefix launch of the shared-prefix decode: the groups' sequence ranges.
   const int32_t *query_start_loc;
+  // Shared-prefix decode (launch_shared_prefix). prefix_lens [member_seqs]:
+  // shared prefix tokens of each sequence. The prefix launch (num_seqs =
+  // groups) writes un-normalised partials per (sequence, head) row into
+  // pre_acc [member_seqs * n_heads, head_dim] and pre_ml; the suffix launch
+  // (num_seqs = sequences) walks tokens [prefix_lens[s], seq_lens[s]) and folds
+  // them in.
+  const int32_t *prefix_lens;
+  int32_t member_seqs;
+  float *pre_acc;
+  float2 *pre_ml;
+  // Shared-prefix decode in one launch (launch_shared_fused): num_seqs counts
+  // entities (num_groups prefixes, then member_seqs private parts); prefix
+  // entities are split into partitions of prefix_partition_tokens, private
+  // ones of partition_tokens; max_parts is the slot stride per (sequence,
+  // head) row (prefix slots first), at most kFusedMergeParts.
+  int32_t num_groups;
+  int32_t prefix_partition_tokens;  // the shortest allowed (the kernel may lengthen it)
+  int32_t prefix_partition_fixed;   // nonzero: use prefix_partition_tokens as given
 };
 
 // Largest partition count merged inside the decode kernel; longer tables use
 // a separate merge kernel.
 constexpr int kFusedMergeParts = 8;
+
+// Decode workgroups resident per compute unit (the kernel's register budget
+// allows three), and the compute units of the current device.
+constexpr int kDecodeWgsPerCu = 3;
+int device_cus();
 
 // Head tile: query heads of one KV head processed by one workgroup (1, 2, 4, 8 or 16).
 int decode_head_tile(int group);
@@ -89,6 +113,18 @@ hipError_t launch_chunk(DType dt, int head_dim, const ChunkArgs &a, hipStream_t 
 // pairs per item, split along the sequence and merged like decode); dt is
 // F16 or BF16; fp8 selects e4m3 pools with a.k_scale / a.v_scale.
 hipError_t launch_chunk_rows(DType dt, int head_dim, bool fp8, const DecodeArgs &a, hipStream_t stream);
+
+// Shared-prefix decode: the prefix launch (pre: rows mode over groups, head
+// tile 16) then the suffix launch (suf: decode of the private tokens with the
+// prefix partials folded in); dt is F16 or BF16.
+hipError_t launch_shared_prefix(DType dt, int head_dim, const DecodeArgs &pre, const DecodeArgs &suf,
+                                hipStream_t stream);
+
+// Shared-prefix decode in one launch: prefix and private partitions are work
+// items of one grid, merged per (sequence, KV head) by the last to finish.
+// Needs n_heads / n_kv_heads in {1, 2, 4, 8, 16} and every group's members x
+// heads per KV head <= 16; dt is F16 or BF16.
+hipError_t launch_shared_fused(DType dt, int head_dim, const DecodeArgs &a, hipStream_t stream);
 
 // Same over FP8 (OCP e4m3) pools with a.k_scale / a.v_scale; dt (query and
 // output) must be F16 or BF16.

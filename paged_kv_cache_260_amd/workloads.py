@@ -202,6 +202,69 @@ def build(
     )
 
 
+def build_groups(*, name: str, rng: np.random.Generator, group_sizes: Sequence[int],
+                 prefix_blocks: Sequence[int], private_lens: Sequence[int], n_heads: int, n_kv_heads: int,
+                 head_dim: int, block_size: int, dtype: torch.dtype, pool_factor: float = 1.3,
+                 poison: bool = False, seed: int = 0) -> Workload:
+    """A batch of consecutive sequence groups: group ``i`` has ``group_sizes[i]``
+    members whose tables start with the same ``prefix_blocks[i]`` physical
+    blocks (full of prefix tokens); member ``s`` then holds
+    ``private_lens[s]`` tokens of its own in private blocks, so
+    ``seq_lens[s] = prefix_blocks[group] * block_size + private_lens[s]``.
+    Physical ids are a random permutation of the pool; ``poison`` fills every
+    slot no sequence may read with NaN."""
+    BS = block_size
+    sizes = [int(x) for x in group_sizes]
+    pblk = [int(x) for x in prefix_blocks]
+    priv = [int(x) for x in private_lens]
+    B = sum(sizes)
+    if len(pblk) != len(sizes) or len(priv) != B:
+        raise ValueError("one prefix per group, one private length per sequence")
+    group_of = np.repeat(np.arange(len(sizes)), sizes)
+    seq_lens = np.array([pblk[group_of[s]] * BS + priv[s] for s in range(B)], dtype=np.int64)
+    mb = max(1, -(-(int(seq_lens.max()) + 1) // BS)) if B else 1
+    private_blocks = [-(-(priv[s] + 1) // BS) for s in range(B)]
+    need = sum(pblk) + sum(private_blocks)
+    num_blocks = int(math.ceil(pool_factor * need))
+    perm = rng.permutation(num_blocks).astype(np.int64)
+    tables = np.full((B, mb), -1, dtype=np.int32)
+    refcount = np.zeros(num_blocks, dtype=np.int32)
+    cursor = 0
+    prefix_ids = []
+    for n in pblk:
+        prefix_ids.append(perm[cursor: cursor + n].tolist())
+        cursor += n
+    for s in range(B):
+        ids = prefix_ids[group_of[s]] + perm[cursor: cursor + private_blocks[s]].tolist()
+        cursor += private_blocks[s]
+        tables[s, : len(ids)] = ids
+        refcount[ids] += 1
+    H, Hkv, D = n_heads, n_kv_heads, head_dim
+    q = _normal(rng, (B, H, D), dtype)
+    k_pool = _normal(rng, (num_blocks, Hkv, BS, D), dtype)
+    v_pool = _normal(rng, (num_blocks, Hkv, BS, D), dtype)
+    k_new = _normal(rng, (B, Hkv, D), dtype)
+    v_new = _normal(rng, (B, Hkv, D), dtype)
+    slots = np.array([int(tables[s, int(seq_lens[s]) // BS]) * BS + int(seq_lens[s]) % BS for s in range(B)],
+                     dtype=np.int32)
+    if poison:
+        nan = float("nan")
+        unused = torch.from_numpy(refcount == 0)
+        k_pool[unused] = nan
+        v_pool[unused] = nan
+        for s in range(B):
+            L = int(seq_lens[s])
+            blk = int(tables[s, L // BS])
+            k_pool[blk, :, L % BS:, :] = nan
+            v_pool[blk, :, L % BS:, :] = nan
+    return Workload(
+        name=name, dtype=dtype, num_seqs=B, n_heads=H, n_kv_heads=Hkv, head_dim=D, block_size=BS,
+        scale=_f32_scale(D), seq_lens=seq_lens.astype(np.int32), block_tables=tables, num_blocks=num_blocks,
+        q=q, k_pool=k_pool, v_pool=v_pool, k_new=k_new, v_new=v_new, slot_mapping=slots,
+        refcount=refcount, seed=seed,
+    )
+
+
 CONFIG_NAMES = {
     1: "tiny fp32 paged decode, B=4, H=Hkv=4, D=64, BS=16, L~U[1,100], pool 32",
     2: "MHA bf16 paged decode, B=64, H=Hkv=32, D=128, BS=16, L~U[128,2048]",
