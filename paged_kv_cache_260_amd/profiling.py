@@ -31,7 +31,8 @@ import os
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-DECODE_SRC = os.path.join(PKG, "csrc", "decode.hip")
+# sources that define the decode kernel's code
+DECODE_SRCS = tuple(os.path.join(PKG, "csrc", f) for f in ("decode.hip", "attn_common.h", "kernels.h"))
 DECODE_KERNEL = "paged_decode_kernel"
 MERGE_KERNEL = "paged_decode_reduce_kernel"
 MERGE_FEW_KERNEL = "paged_decode_merge_few_kernel"
@@ -41,14 +42,26 @@ COPY_KERNEL = "copyBuffer"
 CALL_KERNELS = (DECODE_KERNEL, MERGE_KERNEL, MERGE_FEW_KERNEL)
 
 
-def source_hash(path: str = DECODE_SRC) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(paths=DECODE_SRCS) -> str:
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# the decode kernel's last template argument: what its work items' rows are
+_DECODE_MODES = {"0": "", "1": " (chunk rows)", "2": " (shared prefix)", "3": " (private tokens)",
+                 "4": " (shared prefix, one launch)"}
 
 
 def short_name(name: str) -> str:
-    for key in (*CALL_KERNELS, "kv_cache_write_kernel", "zero_i32_kernel", COPY_KERNEL):
+    for key in (*CALL_KERNELS, "paged_chunk_reduce_kernel", "paged_chunk_kernel", "kv_cache_write_kernel",
+                "zero_i32_kernel", "copy_blocks_kernel", COPY_KERNEL):
         if key in name:
+            if key == DECODE_KERNEL and name.endswith("EEEvNS_10DecodeArgsE") and "ELi" in name:
+                mode = name[: -len("EEEvNS_10DecodeArgsE")].rsplit("ELi", 1)[-1]
+                return key + _DECODE_MODES.get(mode, "")
             return key
     return name[:60]
 
