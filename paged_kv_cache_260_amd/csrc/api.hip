@@ -392,7 +392,8 @@ int pkv_paged_attn_chunk(void *out, const void *q, const void *k_pool, const voi
   a.block_shift = bshift;
   a.max_blocks = max_blocks_per_seq;
   a.num_blocks = num_blocks;
-  a.row_blocks = (int32_t)row_blocks;
+  a.row_blocks = (int32_t)(((int64_t)max_query_len * group + pkv::chunk_rows_per_block() - 1) /
+                           pkv::chunk_rows_per_block());
   hipError_t e = pkv::launch_chunk(static_cast<pkv::DType>(dtype), head_dim, a, st);
   if (e != hipSuccess) return hip_fail(e, "chunk attention launch");
   return ok();

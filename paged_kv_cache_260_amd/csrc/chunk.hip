@@ -1,32 +1,39 @@
 // Paged attention of a chunk of new query tokens per sequence, causal inside
-// the chunk, for CDNA4 (gfx950).
+// the chunk, for CDNA4 (gfx950): the kernel for long chunks (chunked prefill).
 //
 // What is computed: the chunk of sequence s holds its last n_s = qsl[s+1] -
 // qsl[s] tokens (their K/V already in the cache, L_s tokens in all). Chunk
 // token i sits at position p = L_s - n_s + i and attends, per query head,
-// over the cached tokens 0 .. p. n_s = 1 is a decode step and n_s = L_s a
-// whole causal prefill. Sources: chunked prefill (Sarathi-Serve, on the
-// PagedAttention notes page); speculative decoding, whose target model scores
-// several draft tokens at once, and continuous batching, where packed
-// sequences keep to their own tokens through positions and the attention mask
-// (vLLM notes page, scheduling and speculative-decoding sections).
+// over the cached tokens 0 .. p. Sources: chunked prefill (Sarathi-Serve, on
+// the PagedAttention notes page); continuous batching, where packed sequences
+// keep to their own tokens through positions and the attention mask (vLLM
+// notes page, scheduling section); the exact tiled softmax of FlashAttention
+// (vLLM notes page, "FlashAttention").
 //
-// Work decomposition: one 4-wave workgroup per (KV head g, sequence s, block
-// of 16 query rows). Rows are (chunk token, query head of g) pairs,
-// token-major: row r is token r / G, head g * G + r % G. So a speculative
-// chunk of 4 tokens with 4 heads per KV head fills exactly one MFMA row tile.
-// The workgroup walks the causal context in segments of at most 64 blocks
-// (their table entries sit one per lane in a VGPR). Inside a segment the
-// 16-token tiles go round-robin to the waves, as in the decode kernel.
-//
-// Per tile, per wave:
-//   1. Load the K and V tiles, one tile ahead.
-//   2. Stage them in swizzled wave-private LDS.
-//   3. S = Q K^T on v_mfma_f32_16x16x32 (Q, 16 rows, from LDS).
-//   4. Mask tokens past each row's position.
-//   5. Online softmax in base 2 with the lazy reference max.
-//   6. P (hi + lo) and V^T through ds_read_b64_tr_b16 into v_mfma_f32_16x16x16.
-// The four waves' states are merged through LDS at the end.
+// Long chunks make this a dense contraction: every K/V tile meets many query
+// rows. One workgroup (4 waves) takes 128 query rows of one KV head: rows are
+// (chunk token, query head of g) pairs, token-major, so the G heads of one
+// token and 128 / G consecutive tokens share each K/V tile. The context is
+// walked in 64-token stages:
+//   1. The stage's K and V rows (64 x head_dim each) are loaded by the whole
+//      workgroup into registers one stage ahead, then written to LDS (K
+//      row-major, V for transposed reads; both XOR-swizzled) in a double
+//      buffer, with one barrier per stage. Block ids come from a 64-entry
+//      window of the block table held one per lane.
+//   2. Each wave owns 32 rows (two 16-row MFMA tiles) and computes the
+//      transposed scores S^T = K Q^T with v_mfma_f32_16x16x32: Q stays in
+//      registers as the B operand, K is the A operand read from LDS. Lane
+//      (kg, n) receives tokens 4 kg .. 4 kg + 3 of row n in each 16-token
+//      block.
+//   3. Online softmax in base 2 with a lazy reference max (raised only when a
+//      score passes it by more than 8); the causal mask is applied only in
+//      stages that reach past a row's position.
+//   4. O^T += V^T P^T, again on v_mfma_f32_16x16x32: the eight weights a lane
+//      holds for its row (two 16-token blocks) are exactly its B operand for
+//      32 tokens (both operands list the tokens in the same order, which is
+//      all a contraction needs), and V^T comes from LDS through
+//      ds_read_b64_tr_b16.
+// P is rounded to the 16-bit type for the product (accumulation is fp32).
 #include "attn_common.h"
 #include "kernels.h"
 
@@ -37,280 +44,299 @@ namespace {
 
 using namespace attn;
 
-constexpr int kChunkWaves = 4;
-constexpr int kChunkRows = 16;
-constexpr int kSegBlocks = 64;
+constexpr int kPfWaves = 4;
+constexpr int kPfRowsPerWave = 32;
+constexpr int kPfRows = kPfWaves * kPfRowsPerWave;  // 128 query rows per workgroup
+constexpr int kPfStage = 64;                         // context tokens per stage
 
-template <typename T, int D> struct ChunkCfg {
-  static constexpr int kEpc = Elem<T>::kPerChunk;
-  static constexpr int kCh = D / kEpc;                   // 16-byte chunks per token row
-  static constexpr int kLoads = kTileTokens * kCh / 64;  // 16-byte loads per lane per tile
-  static constexpr int kSteps = kCh / 4;                 // QK MFMA steps per tile
-  static constexpr int kDimBlocks = D / 16;
-  static constexpr int kNW = kChunkWaves;
-  static constexpr int kKstBytes = kTileTokens * kCh * 16;
-  static constexpr int kVstBytes = kTileTokens * kCh * 16;
-  static constexpr int kPstBytes = 2 * 16 * 16 * 2;
-  static constexpr int kStageBytes = kKstBytes + kVstBytes + kPstBytes;
-  static constexpr int kAccBytes = kChunkRows * D * 4;
-  static constexpr int kWaveBytes = kStageBytes > kAccBytes ? kStageBytes : kAccBytes;
-  static constexpr int kMlOff = kNW * kWaveBytes;
-  static constexpr int kBadOff = kMlOff + kNW * kChunkRows * 8;
-  static constexpr int kQOff = (kBadOff + kNW * 4 + 15) / 16 * 16;
-  static constexpr int kQChunks = kChunkRows * kCh;
-  static constexpr int kSmem = kQOff + kQChunks * 16;
+template <typename T, int D> struct PfCfg {
+  static constexpr int kCh = D / 8;                                // 16-byte chunks per token row
+  static constexpr int kSteps = kCh / 4;                           // QK MFMA steps (32 dims each)
+  static constexpr int kDimBlocks = D / 16;                        // 16-dim output blocks
+  static constexpr int kLoads = kPfStage * kCh / (kPfWaves * 64);  // 16-byte loads per thread per tile
+  static constexpr int kTileBytes = kPfStage * kCh * 16;           // one K (or V) stage in LDS
+  static constexpr int kBufBytes = 2 * kTileBytes;                 // K + V
+  static constexpr int kSmem = 2 * kBufBytes;                      // double buffer
   static_assert(sizeof(T) == 2 && (kCh == 8 || kCh == 16), "16-bit types, head_dim 64 or 128");
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
-void paged_chunk_kernel(ChunkArgs a) {
-  using C = ChunkCfg<T, D>;
-  constexpr int kL = C::kLoads;
-  constexpr int kCh = C::kCh;
-  constexpr int kNW = C::kNW;
-  __shared__ __attribute__((aligned(16))) char smem[C::kSmem];
+// two floats -> two elements of T (round to nearest even) in one word
+template <typename T> __device__ __forceinline__ uint32_t pack2(float a, float b) {
+  const T x = static_cast<T>(a), y = static_cast<T>(b);
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = (int)(blockIdx.x % (unsigned)a.n_kv_heads);
-  const int rr = (int)(blockIdx.x / (unsigned)a.n_kv_heads);
-  const int rb = rr % a.row_blocks;
-  const int s = rr / a.row_blocks;
+template <typename T, int D>
+__global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void paged_chunk_kernel(ChunkArgs a) {
+  using C = PfCfg<T, D>;
+  constexpr int kCh = C::kCh;
+  constexpr int kL = C::kLoads;
+  constexpr int kDB = C::kDimBlocks;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = lane >> 4;
+  const int n = lane & 15;
+  // work item: row blocks of later chunk tokens (more context) first
+  const int items_per_rb = a.n_kv_heads * a.num_seqs;
+  const int rb = a.row_blocks - 1 - (int)(blockIdx.x / (unsigned)items_per_rb);
+  const int rem = (int)(blockIdx.x % (unsigned)items_per_rb);
+  const int g = rem % a.n_kv_heads;
+  const int s = rem / a.n_kv_heads;
   const int G = a.group;
   const int H = a.n_heads;
   const int q0 = a.query_start_loc[s];
   const int nq = a.query_start_loc[s + 1] - q0;
   const int L = a.seq_lens[s];
-  const int row0 = rb * kChunkRows;
+  const int row0 = rb * kPfRows;
   if (nq <= 0 || q0 < 0 || row0 >= nq * G) return;
-  const int nrows = min(kChunkRows, nq * G - row0);
+  const int nrows = min(kPfRows, nq * G - row0);
   T *out = static_cast<T *>(a.out);
-  const int kg = lane >> 4;
-  const int n = lane & 15;
-
-  auto row_token = [&](int i) { return (row0 + i) / G; };
-  auto row_head = [&](int i) { return g * G + (row0 + i) % G; };
+  auto out_row = [&](int r) -> int64_t {  // r: row within the item
+    const int rr = row0 + r;
+    return (int64_t)(q0 + rr / G) * H + g * G + rr % G;
+  };
 
   const bool bad_len = L < nq || (int64_t)L > (int64_t)a.max_blocks * a.block_size;
   if (bad_len) {
-    for (int i = threadIdx.x; i < nrows * D; i += kNW * 64) {
-      const int r = i / D;
-      out[((int64_t)(q0 + row_token(r)) * H + row_head(r)) * D + i % D] = static_cast<T>(__builtin_nanf(""));
-    }
+    for (int i = tid; i < nrows * D; i += kPfWaves * 64)
+      out[out_row(i / D) * D + i % D] = static_cast<T>(__builtin_nanf(""));
     return;
   }
-  // positions: row i sees tokens 0 .. L - nq + token(i); the block's context
-  // ends after its last row's position
-  const int base_pos = L - nq;
-  const int ctx_end = base_pos + row_token(nrows - 1) + 1;
-  int lim[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = 4 * kg + r;
-    lim[r] = i < nrows ? base_pos + row_token(i) : -1;
-  }
+  const int base_pos = L - nq;                                // position of chunk token 0
+  const int ctx_end = base_pos + (row0 + nrows - 1) / G + 1;  // tokens the item's rows may see
 
-  // Q rows -> LDS (swizzled like a K tile), zero past nrows
-  {
-    u32x4_t *qs = reinterpret_cast<u32x4_t *>(smem + C::kQOff);
-    for (int u = threadIdx.x; u < C::kQChunks; u += kNW * 64) {
-      const int i = u / kCh;
-      const int c = u - i * kCh;
-      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-      if (i < nrows)
-        v = reinterpret_cast<const u32x4_t *>(static_cast<const T *>(a.q) +
-                                              ((int64_t)(q0 + row_token(i)) * H + row_head(i)) * D)[c];
-      qs[kst_slot<kCh>(i, c)] = v;
+  // this lane's rows (one per row tile) and their last visible positions;
+  // rows past nrows (padding) take the last row's position
+  const int wrow0 = wave * kPfRowsPerWave;
+  int rpos[2];
+  bool rvalid[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int r = wrow0 + 16 * rt + n;
+    rvalid[rt] = r < nrows;
+    rpos[rt] = base_pos + (row0 + min(r, nrows - 1)) / G;
+  }
+  // smallest position among the wave's rows: stages up to it need no mask
+  const int wave_min_pos = base_pos + (row0 + min(wrow0, nrows - 1)) / G;
+
+  // Q operand (B of S^T = K Q^T): lane (kg, n) holds chunk 4 c + kg of row n
+  u32x4_t qb[2][C::kSteps];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int r = wrow0 + 16 * rt + n;
+#pragma unroll
+    for (int c = 0; c < C::kSteps; ++c) {
+      qb[rt][c] = u32x4_t{0u, 0u, 0u, 0u};
+      if (r < nrows)
+        qb[rt][c] = reinterpret_cast<const u32x4_t *>(static_cast<const T *>(a.q) + out_row(r) * D)[4 * c + kg];
     }
   }
-  __syncthreads();
-  const u32x4_t *qs = reinterpret_cast<const u32x4_t *>(smem + C::kQOff);
-
-  char *wreg = smem + wave * C::kWaveBytes;
-  u32x4_t *kst = reinterpret_cast<u32x4_t *>(wreg);
-  char *vst = wreg + C::kKstBytes;
-  char *pst = wreg + C::kKstBytes + C::kVstBytes;
-  for (int i = lane; i < 2 * 16 * 16 / 8; i += 64) reinterpret_cast<uint2 *>(pst)[i] = make_uint2(0u, 0u);
 
   const int64_t kv_stride_blk = (int64_t)a.n_kv_heads * a.block_size;
   const int32_t *bt_row = a.block_tables + (int64_t)s * a.max_blocks;
   const u32x4_t *kbase = static_cast<const u32x4_t *>(a.k_pool);
   const u32x4_t *vbase = static_cast<const u32x4_t *>(a.v_pool);
+  const int nst = (ctx_end + kPfStage - 1) / kPfStage;
+  // block-table window: lane i holds entry win + i (a stage spans at most 4
+  // blocks, so it always fits one window)
+  int win = 0;
+  int btv = lane < a.max_blocks ? bt_row[lane] : 0;
   bool bad = false;
+
   struct Regs {
     u32x4_t k[kL];
     u32x4_t v[kL];
   };
-
-  float m[4], l[4];
+  // loads of stage st into registers: thread chunk u = tid + 256 i is chunk
+  // u % kCh of token u / kCh; tokens at or past ctx_end stay zero
+  auto load_stage = [&](int st, Regs &rg) {
+    const int t0 = st * kPfStage;
+    const int last_blk = (min(t0 + kPfStage, ctx_end) - 1) >> a.block_shift;
+    if (last_blk >= win + 64) {  // uniform: move the window to this stage
+      win = t0 >> a.block_shift;
+      btv = win + lane < a.max_blocks ? bt_row[win + lane] : 0;
+    }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m[r] = -INFINITY;
-    l[r] = 0.f;
-  }
-  f32x4_t acc[C::kDimBlocks];
+    for (int i = 0; i < kL; ++i) {
+      const int u = tid + i * kPfWaves * 64;
+      const int tok = t0 + u / kCh;
+      rg.k[i] = rg.v[i] = u32x4_t{0u, 0u, 0u, 0u};
+      const int j = (min(tok, ctx_end - 1) >> a.block_shift) - win;  // 0 .. 63
+      int phys = __shfl(btv, j, 64);
+      if (tok < ctx_end) {
+        if (phys < 0 || (int64_t)phys >= a.num_blocks) {
+          bad = true;
+          phys = 0;
+        }
+        const int64_t off = ((int64_t)phys * kv_stride_blk + (int64_t)g * a.block_size +
+                             (tok & (a.block_size - 1))) * kCh + u % kCh;
+        rg.k[i] = __builtin_nontemporal_load(kbase + off);
+        rg.v[i] = __builtin_nontemporal_load(vbase + off);
+      }
+    }
+  };
+  auto store_stage = [&](int buf, const Regs &rg) {
+    u32x4_t *ks = reinterpret_cast<u32x4_t *>(smem + buf * C::kBufBytes);
+    u32x4_t *vs = reinterpret_cast<u32x4_t *>(smem + buf * C::kBufBytes + C::kTileBytes);
 #pragma unroll
-  for (int b = 0; b < C::kDimBlocks; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < kL; ++i) {
+      const int u = tid + i * kPfWaves * 64;
+      const int tr = u / kCh;
+      const int ch = u % kCh;
+      ks[kst_slot<kCh>(tr, ch)] = rg.k[i];
+      vs[tr * kCh + (ch ^ vst_swz<kCh>(tr))] = rg.v[i];
+    }
+  };
 
-  const int tr_tok = 4 * kg + ((lane & 15) >> 2);
-  const int p_tr_off = tr_tok * 32 + (lane & 3) * 8;
-  const int v_tr_base = tr_tok * kCh * 16 + (lane & 3) * 8;
-  const int v_tr_swz = vst_swz<kCh>(tr_tok);
+  // running state per row tile: reference max (base 2), this lane's share of
+  // the sum, and O^T accumulators (lane (kg, n): row n, dims 16 b + 4 kg + r)
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  f32x4_t acc[2][kDB];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int b = 0; b < kDB; ++b) acc[rt][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   constexpr float kLazy = 8.f;
+  const float sl2 = a.scale_log2;
+  // transposed V reads: this lane addresses token 4 kg + (n >> 2) of a 16-token block
+  const int tr_tok = 4 * kg + (n >> 2);
+  const int v_tr_off = tr_tok * kCh * 16 + (lane & 3) * 8;
+  const int v_tr_swz = vst_swz<kCh>(tr_tok);
 
-  const int seg_tokens = kSegBlocks * a.block_size;
-  for (int seg = 0; seg < ctx_end; seg += seg_tokens) {
-    const int seg_end = min(ctx_end, seg + seg_tokens);
-    const int jb = seg >> a.block_shift;
-    const int jmax = (seg_end - 1) >> a.block_shift;
-    const int btv = jb + lane <= jmax ? bt_row[jb + lane] : 0;
+  Regs rg;
+  load_stage(0, rg);
+  store_stage(0, rg);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nst) load_stage(st + 1, rg);
+    const u32x4_t *ks = reinterpret_cast<const u32x4_t *>(smem + buf * C::kBufBytes);
+    const char *vs = smem + buf * C::kBufBytes + C::kTileBytes;
+    const int t0 = st * kPfStage;
 
-    auto load_tile = [&](int ti, Regs &rg) {
-      const int tok = ti * kTileTokens;
-      int phys = __builtin_amdgcn_readlane(btv, (tok >> a.block_shift) - jb);
-      if (phys < 0 || (int64_t)phys >= a.num_blocks) {
-        bad = true;
-        phys = 0;
+    // S^T = K Q^T for 4 token blocks x 2 row tiles
+    f32x4_t sc[4][2];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      sc[tb][0] = sc[tb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < C::kSteps; ++c) {
+        const u32x4_t kop = ks[kst_slot<kCh>(tb * 16 + n, 4 * c + kg)];
+        sc[tb][0] = mfma_chunk<T>(kop, qb[0][c], sc[tb][0]);
+        sc[tb][1] = mfma_chunk<T>(kop, qb[1][c], sc[tb][1]);
       }
-      const int64_t off = ((int64_t)phys * kv_stride_blk + (int64_t)g * a.block_size +
-                           (tok & (a.block_size - 1))) * kCh;
+    }
+    const bool masked = t0 + kPfStage - 1 > wave_min_pos;  // uniform
+    u32x4_t pt[2][2];  // P^T operands: [row tile][32-token half]
 #pragma unroll
-      for (int i = 0; i < kL; ++i) rg.k[i] = kbase[off + i * 64 + lane];
-#pragma unroll
-      for (int i = 0; i < kL; ++i) rg.v[i] = vbase[off + i * 64 + lane];
-    };
-
-    auto process = [&](int ti, Regs &rg, int next) {
-      const int valid = seg_end - ti * kTileTokens;  // tokens of this tile inside the context
-      u32x4_t *vs = reinterpret_cast<u32x4_t *>(vst);
-#pragma unroll
-      for (int i = 0; i < kL; ++i) {
-        const int u = i * 64 + lane;
-        const int tr = u / kCh;
-        kst[kst_slot<kCh>(tr, u % kCh)] = rg.k[i];
-        // rows past the context are zeroed: 0 * NaN would poison the sums
-        vs[tr * kCh + ((u % kCh) ^ vst_swz<kCh>(tr))] = tr < valid ? rg.v[i] : u32x4_t{0u, 0u, 0u, 0u};
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      if (next >= 0) load_tile(next, rg);
-      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < C::kSteps; ++c)
-        sc = mfma_chunk<T>(qs[kst_slot<kCh>(n, kg + 4 * c)], kst[kst_slot<kCh>(n, kg + 4 * c)], sc);
-      const int tok = ti * kTileTokens + n;
-      float z[4];
+    for (int rt = 0; rt < 2; ++rt) {
+      float z[4][4];
       bool over = false;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        z[r] = tok <= lim[r] ? sc[r] * a.scale_log2 : -INFINITY;
-        over |= z[r] > m[r] + kLazy;
-      }
-      if (__builtin_amdgcn_ballot_w64(over) != 0) {
+      for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float mn = fmaxf(m[r], row_max16(z[r]));
-          const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[r] - mn);
-          m[r] = mn;
-          l[r] *= alpha;
-#pragma unroll
-          for (int b = 0; b < C::kDimBlocks; ++b) acc[b][r] *= alpha;
+          const int tok = t0 + tb * 16 + 4 * kg + r;
+          float v = sc[tb][rt][r] * sl2;
+          if (masked) v = tok <= rpos[rt] ? v : -INFINITY;
+          z[tb][r] = v;
+          over |= v > m[rt] + kLazy;
         }
+      if (__builtin_amdgcn_ballot_w64(over) != 0) {  // uniform: raise the reference
+        float mx = z[0][0];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, z[tb][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mn = fmaxf(m[rt], mx);
+        const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[rt] - mn);
+        m[rt] = mn;
+        l[rt] *= alpha;
+#pragma unroll
+        for (int b = 0; b < kDB; ++b) acc[rt][b] *= alpha;
       }
-      float p[4];
+      float p[4][4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[r] = z[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[r] - m[r]);
-        l[r] += p[r];
-      }
-      typename Pv<T>::v4 hi, lo;
+      for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        hi[r] = static_cast<T>(p[r]);
-        lo[r] = static_cast<T>(p[r] - static_cast<float>(hi[r]));
-      }
-      *reinterpret_cast<typename Pv<T>::v4 *>(pst + n * 32 + kg * 8) = hi;
-      *reinterpret_cast<typename Pv<T>::v4 *>(pst + 512 + n * 32 + kg * 8) = lo;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const typename Pv<T>::v4 pa_hi = lds_read_tr<T>(pst + p_tr_off);
-      const typename Pv<T>::v4 pa_lo = lds_read_tr<T>(pst + 512 + p_tr_off);
+        for (int r = 0; r < 4; ++r) {
+          const float e = __builtin_amdgcn_exp2f(z[tb][r] - m[rt]);
+          p[tb][r] = z[tb][r] == -INFINITY ? 0.f : e;
+          l[rt] += p[tb][r];
+        }
 #pragma unroll
-      for (int b = 0; b < C::kDimBlocks; ++b) {
-        const typename Pv<T>::v4 vb = lds_read_tr<T>(vst + v_tr_base + (((2 * b) ^ v_tr_swz) << 4));
-        acc[b] = Pv<T>::mfma(pa_hi, vb, acc[b]);
-        acc[b] = Pv<T>::mfma(pa_lo, vb, acc[b]);
-      }
-    };
-
-    const int tb = seg / kTileTokens;
-    const int te = (seg_end + kTileTokens - 1) / kTileTokens;
-    Regs rg;
-    int ti = tb + wave;
-    if (ti < te) load_tile(ti, rg);
-    for (; ti < te; ti += kNW) process(ti, rg, ti + kNW < te ? ti + kNW : -1);
-  }
-
-  // ---- merge the four waves through LDS
-#pragma unroll
-  for (int r = 0; r < 4; ++r) l[r] = row_sum16(l[r]);
-  __syncthreads();  // every wave is done with its staging area
-  float *macc = reinterpret_cast<float *>(wreg);
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int b = 0; b < C::kDimBlocks; ++b) macc[(4 * kg + r) * D + 16 * b + n] = acc[b][r];
-  float2 *mml = reinterpret_cast<float2 *>(smem + C::kMlOff) + wave * kChunkRows;
-  if (n == 0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mml[4 * kg + r] = make_float2(m[r], l[r]);
-  }
-  int *mbad = reinterpret_cast<int *>(smem + C::kBadOff);
-  if (lane == 0) mbad[wave] = bad ? 1 : 0;
-  __syncthreads();
-  const float2 *ml_all = reinterpret_cast<const float2 *>(smem + C::kMlOff);
-  int any_bad = 0;
-#pragma unroll
-  for (int w = 0; w < kNW; ++w) any_bad |= mbad[w];
-  for (int idx = threadIdx.x; idx < nrows * D; idx += kNW * 64) {
-    const int i = idx / D;
-    const int d = idx - i * D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kNW; ++w) M = fmaxf(M, ml_all[w * kChunkRows + i].x);
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int w = 0; w < kNW; ++w) {
-      const float2 ml = ml_all[w * kChunkRows + i];
-      const float f = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
-      den = fmaf(f, ml.y, den);
-      num = fmaf(f, reinterpret_cast<const float *>(smem + w * C::kWaveBytes)[i * D + d], num);
+      for (int h = 0; h < 2; ++h)
+        pt[rt][h] = u32x4_t{pack2<T>(p[2 * h][0], p[2 * h][1]), pack2<T>(p[2 * h][2], p[2 * h][3]),
+                            pack2<T>(p[2 * h + 1][0], p[2 * h + 1][1]), pack2<T>(p[2 * h + 1][2], p[2 * h + 1][3])};
     }
-    out[((int64_t)(q0 + row_token(i)) * H + row_head(i)) * D + d] =
-        static_cast<T>(any_bad ? __builtin_nanf("") : num / den);
+    // O^T += V^T P^T: 32 tokens (two 16-token blocks) per MFMA
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int b = 0; b < kDB; ++b) {
+        const int cofs = ((2 * b) ^ v_tr_swz) << 4;
+        const auto v0 = lds_read_tr<T>(vs + (2 * h) * 16 * kCh * 16 + v_tr_off + cofs);
+        const auto v1 = lds_read_tr<T>(vs + (2 * h + 1) * 16 * kCh * 16 + v_tr_off + cofs);
+        const uint2 w0 = __builtin_bit_cast(uint2, v0);
+        const uint2 w1 = __builtin_bit_cast(uint2, v1);
+        const u32x4_t vop = u32x4_t{w0.x, w0.y, w1.x, w1.y};
+        acc[0][b] = mfma_chunk<T>(vop, pt[0][h], acc[0][b]);
+        acc[1][b] = mfma_chunk<T>(vop, pt[1][h], acc[1][b]);
+      }
+    }
+    if (st + 1 < nst) store_stage(buf ^ 1, rg);
+    __syncthreads();
   }
+
+  // ---- finalize: row sums over the four lanes of a row, then O = acc / l
+  const int any_bad = __syncthreads_or(bad ? 1 : 0);
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    float lt = l[rt];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    const float inv = 1.f / lt;
+    if (!rvalid[rt]) continue;
+    T *orow = out + out_row(wrow0 + 16 * rt + n) * D;
+#pragma unroll
+    for (int b = 0; b < kDB; ++b) {
+      const float nan = __builtin_nanf("");
+      uint2 w;
+      w.x = pack2<T>(any_bad ? nan : acc[rt][b][0] * inv, any_bad ? nan : acc[rt][b][1] * inv);
+      w.y = pack2<T>(any_bad ? nan : acc[rt][b][2] * inv, any_bad ? nan : acc[rt][b][3] * inv);
+      *reinterpret_cast<uint2 *>(orow + 16 * b + 4 * kg) = w;
+    }
+  }
+}
+
+template <typename T, int D> hipError_t launch_chunk_td(const ChunkArgs &a, hipStream_t stream) {
+  constexpr int kSmem = PfCfg<T, D>::kSmem;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&paged_chunk_kernel<T, D>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kSmem);
+  if (attr != hipSuccess) return attr;
+  const dim3 grid((unsigned)((int64_t)a.n_kv_heads * a.num_seqs * a.row_blocks));
+  hipLaunchKernelGGL((paged_chunk_kernel<T, D>), grid, dim3(kPfWaves * 64), kSmem, stream, a);
+  return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_chunk_t(int head_dim, const ChunkArgs &a, hipStream_t stream) {
-  const dim3 grid((unsigned)((int64_t)a.n_kv_heads * a.num_seqs * a.row_blocks));
   switch (head_dim) {
-    case 64:
-      hipLaunchKernelGGL((paged_chunk_kernel<T, 64>), grid, dim3(kChunkWaves * 64), 0, stream, a);
-      break;
-    case 128:
-      hipLaunchKernelGGL((paged_chunk_kernel<T, 128>), grid, dim3(kChunkWaves * 64), 0, stream, a);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 64: return launch_chunk_td<T, 64>(a, stream);
+    case 128: return launch_chunk_td<T, 128>(a, stream);
+    default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace
+
+int chunk_rows_per_block() { return kPfRows; }
 
 hipError_t launch_chunk(DType dt, int head_dim, const ChunkArgs &a, hipStream_t stream) {
   switch (dt) {

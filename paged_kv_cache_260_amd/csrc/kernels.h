@@ -104,8 +104,11 @@ struct ChunkArgs {
   int32_t block_shift;
   int32_t max_blocks;
   int64_t num_blocks;
-  int32_t row_blocks;              // ceil(max_query_len * group / 16)
+  int32_t row_blocks;              // ceil(max_query_len * group / chunk_rows_per_block())
 };
+
+// Query rows (chunk token x query head pairs) per chunk-kernel workgroup.
+int chunk_rows_per_block();
 
 hipError_t launch_chunk(DType dt, int head_dim, const ChunkArgs &a, hipStream_t stream);
 
