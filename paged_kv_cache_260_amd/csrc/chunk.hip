@@ -11,9 +11,9 @@
 // (vLLM notes page, "FlashAttention").
 //
 // Long chunks make this a dense contraction: every K/V tile meets many query
-// rows. One workgroup (4 waves) takes 128 query rows of one KV head: rows are
+// rows. One workgroup (8 waves) takes 256 query rows of one KV head: rows are
 // (chunk token, query head of g) pairs, token-major, so the G heads of one
-// token and 128 / G consecutive tokens share each K/V tile. The context is
+// token and 256 / G consecutive tokens share each K/V tile. The context is
 // walked in 64-token stages:
 //   1. The stage's K and V rows (64 x head_dim each) are loaded by the whole
 //      workgroup into registers one stage ahead, then written to LDS (K
@@ -44,9 +44,9 @@ namespace {
 
 using namespace attn;
 
-constexpr int kPfWaves = 4;
+constexpr int kPfWaves = 8;
 constexpr int kPfRowsPerWave = 32;
-constexpr int kPfRows = kPfWaves * kPfRowsPerWave;  // 128 query rows per workgroup
+constexpr int kPfRows = kPfWaves * kPfRowsPerWave;  // 256 query rows per workgroup
 constexpr int kPfStage = 64;                         // context tokens per stage
 
 template <typename T, int D> struct PfCfg {
@@ -60,10 +60,12 @@ template <typename T, int D> struct PfCfg {
   static_assert(sizeof(T) == 2 && (kCh == 8 || kCh == 16), "16-bit types, head_dim 64 or 128");
 };
 
-// two floats -> two elements of T (round to nearest even) in one word
+// two floats -> two elements of T (round to nearest even) in one word; a
+// vector conversion, so bf16 takes one v_cvt_pk_bf16_f32
 template <typename T> __device__ __forceinline__ uint32_t pack2(float a, float b) {
-  const T x = static_cast<T>(a), y = static_cast<T>(b);
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  typedef T t2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{a, b}), t2));
 }
 
 template <typename T, int D>
@@ -192,9 +194,13 @@ void paged_chunk_kernel(ChunkArgs a) {
     }
   };
 
-  // running state per row tile: reference max (base 2), this lane's share of
-  // the sum, and O^T accumulators (lane (kg, n): row n, dims 16 b + 4 kg + r)
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  // running state per row tile: reference max (base 2), the weight sums, and
+  // O^T accumulators (lane (kg, n): row n, dims 16 b + 4 kg + r)
+  // lsum[rt]: every element holds row n's sum of weights
+  float m[2] = {-INFINITY, -INFINITY};
+  f32x4_t lsum[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  const uint32_t one2 = pack2<T>(1.f, 1.f);
+  const u32x4_t ones = u32x4_t{one2, one2, one2, one2};
   f32x4_t acc[2][kDB];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
@@ -230,46 +236,55 @@ void paged_chunk_kernel(ChunkArgs a) {
         sc[tb][1] = mfma_chunk<T>(kop, qb[1][c], sc[tb][1]);
       }
     }
-    const bool masked = t0 + kPfStage - 1 > wave_min_pos;  // uniform
     u32x4_t pt[2][2];  // P^T operands: [row tile][32-token half]
+    float z[2][4][4];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) z[rt][tb][r] = sc[tb][rt][r] * sl2;
+    // causal mask, only in the stages that reach past a row's position (a
+    // real branch: the empty asm keeps it from becoming selects everywhere)
+    if (t0 + kPfStage - 1 > wave_min_pos) {
+      asm volatile("");
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            z[rt][tb][r] = t0 + tb * 16 + 4 * kg + r <= rpos[rt] ? z[rt][tb][r] : -INFINITY;
+    }
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-      float z[4][4];
       bool over = false;
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tok = t0 + tb * 16 + 4 * kg + r;
-          float v = sc[tb][rt][r] * sl2;
-          if (masked) v = tok <= rpos[rt] ? v : -INFINITY;
-          z[tb][r] = v;
-          over |= v > m[rt] + kLazy;
-        }
+        for (int r = 0; r < 4; ++r) over |= z[rt][tb][r] > m[rt] + kLazy;
       if (__builtin_amdgcn_ballot_w64(over) != 0) {  // uniform: raise the reference
-        float mx = z[0][0];
+        float mx = z[rt][0][0];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, z[tb][r]);
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, z[rt][tb][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float mn = fmaxf(m[rt], mx);
         const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[rt] - mn);
         m[rt] = mn;
-        l[rt] *= alpha;
+        lsum[rt] *= alpha;
 #pragma unroll
         for (int b = 0; b < kDB; ++b) acc[rt][b] *= alpha;
       }
+      // every row sees token 0 in the first stage, so m is finite from then
+      // on and masked scores give exp2(-inf) = 0 with no test
       float p[4][4];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float e = __builtin_amdgcn_exp2f(z[tb][r] - m[rt]);
-          p[tb][r] = z[tb][r] == -INFINITY ? 0.f : e;
-          l[rt] += p[tb][r];
-        }
+        for (int r = 0; r < 4; ++r) p[tb][r] = __builtin_amdgcn_exp2f(z[rt][tb][r] - m[rt]);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         pt[rt][h] = u32x4_t{pack2<T>(p[2 * h][0], p[2 * h][1]), pack2<T>(p[2 * h][2], p[2 * h][3]),
@@ -289,19 +304,20 @@ void paged_chunk_kernel(ChunkArgs a) {
         acc[0][b] = mfma_chunk<T>(vop, pt[0][h], acc[0][b]);
         acc[1][b] = mfma_chunk<T>(vop, pt[1][h], acc[1][b]);
       }
+      // row sums of the rounded weights on the MFMA (V^T = ones): the same
+      // weights as the numerator, and no per-element adds
+      lsum[0] = mfma_chunk<T>(ones, pt[0][h], lsum[0]);
+      lsum[1] = mfma_chunk<T>(ones, pt[1][h], lsum[1]);
     }
     if (st + 1 < nst) store_stage(buf ^ 1, rg);
     __syncthreads();
   }
 
-  // ---- finalize: row sums over the four lanes of a row, then O = acc / l
+  // ---- finalize: O = acc / sum
   const int any_bad = __syncthreads_or(bad ? 1 : 0);
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    float lt = l[rt];
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
-    const float inv = 1.f / lt;
+    const float inv = 1.f / lsum[rt][0];
     if (!rvalid[rt]) continue;
     T *orow = out + out_row(wrow0 + 16 * rt + n) * D;
 #pragma unroll
