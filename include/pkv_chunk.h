@@ -35,7 +35,10 @@
  * Device-side values are not checked on the host. A sequence with n_s >
  * seq_lens[s], or seq_lens[s] > max_blocks_per_seq * block_size, or a used
  * table entry outside the pool gets NaN rows; chunk rows past max_query_len
- * are not computed.
+ * are not computed. Cached K/V rows must be finite: long chunks multiply
+ * whole 64-token stages with a weight of exactly zero for the tokens a row
+ * may not see, so a NaN or infinity stored at a cached token can also reach
+ * earlier rows of the same chunk (slots past seq_lens[s] are never read).
  */
 #ifndef PKV_CHUNK_H
 #define PKV_CHUNK_H
@@ -52,6 +55,21 @@ PKV_API int pkv_paged_attn_chunk(void *out, const void *q, const void *k_pool, c
                                  int32_t n_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_seqs,
                                  int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_query_len,
                                  int32_t dtype, void *stream);
+
+/*
+ * pkv_paged_attn_chunk over FP8 pools (the format and scales of pkv_fp8.h):
+ * the same result definition, with K and V rows the dequantized values
+ * decode(code) * scale[KV head]. k_pool and v_pool are uint8 [num_blocks,
+ * n_kv_heads, block_size, head_dim]; k_scale and v_scale are device float32
+ * [n_kv_heads]; dtype (of q and out) is PKV_F16 or PKV_BF16. Other arguments
+ * and device-side checks as in pkv_paged_attn_chunk.
+ */
+PKV_API int pkv_paged_attn_chunk_fp8(void *out, const void *q, const void *k_pool, const void *v_pool,
+                                     const float *k_scale, const float *v_scale, const int32_t *block_tables,
+                                     const int32_t *seq_lens, const int32_t *query_start_loc, float scale,
+                                     int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                                     int32_t num_seqs, int32_t max_blocks_per_seq, int64_t num_blocks,
+                                     int32_t max_query_len, int32_t dtype, void *stream);
 
 #ifdef __cplusplus
 }

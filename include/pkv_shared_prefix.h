@@ -77,6 +77,24 @@ PKV_API int pkv_paged_attn_decode_shared_prefix(void *out, const void *q, const 
                                                 int64_t num_blocks, int32_t dtype, void *stream);
 
 /*
+ * pkv_paged_attn_decode_shared_prefix over FP8 pools (the format and scales of
+ * pkv_fp8.h): the same result definition with the dequantized rows
+ * decode(code) * scale[KV head]. k_pool and v_pool are uint8 [num_blocks,
+ * n_kv_heads, block_size, head_dim]; k_scale and v_scale are device float32
+ * [n_kv_heads]; dtype (of q and out) is PKV_F16 or PKV_BF16. Other arguments,
+ * paths and checks as in pkv_paged_attn_decode_shared_prefix.
+ */
+PKV_API int pkv_paged_attn_decode_shared_prefix_fp8(void *out, const void *q, const void *k_pool,
+                                                    const void *v_pool, const float *k_scale, const float *v_scale,
+                                                    const int32_t *block_tables, const int32_t *seq_lens,
+                                                    const int32_t *prefix_lens, const int32_t *group_start,
+                                                    float scale, int32_t n_heads, int32_t n_kv_heads,
+                                                    int32_t head_dim, int32_t block_size, int32_t num_seqs,
+                                                    int32_t num_groups, int32_t max_group_size,
+                                                    int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
+                                                    void *stream);
+
+/*
  * Host helper: a sharing description for pkv_paged_attn_decode_shared_prefix
  * from host copies of the block tables and lengths. Consecutive sequences
  * join one group while they hold the same first table entry (and each has at

@@ -21,9 +21,11 @@ from ._lib import (  # noqa: F401
     kv_cache_write_fp8,
     last_error,
     paged_attn_chunk,
+    paged_attn_chunk_fp8,
     paged_attn_decode,
     paged_attn_decode_fp8,
     paged_attn_decode_shared_prefix,
+    paged_attn_decode_shared_prefix_fp8,
     release_workspace,
     set_partition_tokens,
     shared_prefix_groups,
@@ -38,6 +40,8 @@ __all__ = [
     "paged_attn_chunk",
     "paged_attn_decode_shared_prefix",
     "shared_prefix_groups",
+    "paged_attn_chunk_fp8",
+    "paged_attn_decode_shared_prefix_fp8",
     "kv_cache_write_fp8",
     "kv_cache_write",
     "decode_plan",

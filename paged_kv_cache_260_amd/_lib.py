@@ -58,6 +58,11 @@ _SIGNATURES = {
                                                            _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
                                                            _i32, _vp]),
     "pkv_shared_prefix_groups": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "pkv_paged_attn_decode_shared_prefix_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                               _f32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                               _i32, _i64, _i32, _vp]),
+    "pkv_paged_attn_chunk_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32,
+                                                _i32, _i32, _i32, _i32, _i64, _i32, _i32, _vp]),
     # FP8 (e4m3) KV cache (pkv_fp8.h)
     "pkv_paged_attn_decode_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32,
                                                  _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
@@ -447,3 +452,65 @@ def shared_prefix_groups(block_tables, seq_lens, block_size: int):
                                           gs.ctypes.data, pl.ctypes.data, ctypes.addressof(ng),
                                           ctypes.addressof(mg)))
     return gs[:ng.value + 1].copy() if B else np.zeros(1, np.int32), pl, mg.value
+
+
+def _fp8_pools(k_pool, v_pool, k_scale, v_scale, n_kv_heads, block_size, head_dim):
+    for name, t in (("k_pool", k_pool), ("v_pool", v_pool)):
+        _dev_tensor(t, name, torch.uint8)
+    _need(k_pool.dim() == 4 and k_pool.shape[1:] == (n_kv_heads, block_size, head_dim),
+          "k_pool must be uint8 [NB, Hkv, BS, D]")
+    _need(v_pool.shape == k_pool.shape, "v_pool must match k_pool")
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        _dev_tensor(t, name, torch.float32)
+        _need(t.shape == (n_kv_heads,), f"{name} must be float32 [n_kv_heads]")
+
+
+def paged_attn_chunk_fp8(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, seq_lens, query_start_loc,
+                         scale: float, n_heads: int, n_kv_heads: int, head_dim: int, block_size: int,
+                         max_query_len: int, stream=None):
+    """:func:`paged_attn_chunk` over FP8 (e4m3) pools with per-KV-head float32 scales."""
+    dt = q.dtype
+    _need(dt in (torch.float16, torch.bfloat16), f"chunk attention needs fp16/bf16 queries, got {dt}")
+    _dev_tensor(out, "out", dt)
+    _dev_tensor(q, "q", dt)
+    _fp8_pools(k_pool, v_pool, k_scale, v_scale, n_kv_heads, block_size, head_dim)
+    for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens), ("query_start_loc", query_start_loc)):
+        _dev_tensor(t, name, torch.int32)
+    B = seq_lens.shape[0]
+    _need(q.dim() == 3 and q.shape[1:] == (n_heads, head_dim) and out.shape == q.shape, "q/out must be [T, H, D]")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B, MB]")
+    _need(query_start_loc.shape == (B + 1,), "query_start_loc must be [B + 1]")
+    with torch.cuda.device(q.device):
+        _check(lib().pkv_paged_attn_chunk_fp8(
+            out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_scale.data_ptr(),
+            v_scale.data_ptr(), block_tables.data_ptr(), seq_lens.data_ptr(), query_start_loc.data_ptr(),
+            float(scale), n_heads, n_kv_heads, head_dim, block_size, B, block_tables.shape[1], k_pool.shape[0],
+            int(max_query_len), DTYPE_CODES[dt], _stream_handle(q, stream)))
+    return out
+
+
+def paged_attn_decode_shared_prefix_fp8(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, seq_lens,
+                                        prefix_lens, group_start, scale: float, n_heads: int, n_kv_heads: int,
+                                        head_dim: int, block_size: int, max_group_size: int, stream=None):
+    """:func:`paged_attn_decode_shared_prefix` over FP8 (e4m3) pools with per-KV-head float32 scales."""
+    dt = q.dtype
+    _need(dt in (torch.float16, torch.bfloat16), f"shared-prefix decode needs fp16/bf16 queries, got {dt}")
+    _dev_tensor(out, "out", dt)
+    _dev_tensor(q, "q", dt)
+    _fp8_pools(k_pool, v_pool, k_scale, v_scale, n_kv_heads, block_size, head_dim)
+    for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens), ("prefix_lens", prefix_lens),
+                    ("group_start", group_start)):
+        _dev_tensor(t, name, torch.int32)
+    B = seq_lens.shape[0]
+    _need(q.shape == (B, n_heads, head_dim) and out.shape == q.shape, "q/out must be [B, H, D]")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B, MB]")
+    _need(prefix_lens.shape == (B,), "prefix_lens must be [B]")
+    _need(group_start.dim() == 1 and group_start.shape[0] >= 2, "group_start must be [G + 1]")
+    with torch.cuda.device(q.device):
+        _check(lib().pkv_paged_attn_decode_shared_prefix_fp8(
+            out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_scale.data_ptr(),
+            v_scale.data_ptr(), block_tables.data_ptr(), seq_lens.data_ptr(), prefix_lens.data_ptr(),
+            group_start.data_ptr(), float(scale), n_heads, n_kv_heads, head_dim, block_size, B,
+            group_start.shape[0] - 1, int(max_group_size), block_tables.shape[1], k_pool.shape[0],
+            DTYPE_CODES[dt], _stream_handle(q, stream)))
+    return out

@@ -303,11 +303,16 @@ int pkv_paged_attn_decode_fp8(void *out, const void *q, const void *k_pool, cons
                      v_scale);
 }
 
-int pkv_paged_attn_chunk(void *out, const void *q, const void *k_pool, const void *v_pool,
-                         const int32_t *block_tables, const int32_t *seq_lens, const int32_t *query_start_loc,
-                         float scale, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
-                         int32_t num_seqs, int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_query_len,
-                         int32_t dtype, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by the 16-bit and the FP8 chunk entry points.
+int chunk_impl(void *out, const void *q, const void *k_pool, const void *v_pool, const int32_t *block_tables,
+               const int32_t *seq_lens, const int32_t *query_start_loc, float scale, int32_t n_heads,
+               int32_t n_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_seqs,
+               int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_query_len, int32_t dtype, void *stream,
+               bool fp8, const float *k_scale, const float *v_scale) {
   if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID, "unknown dtype %d", dtype);
   if (dtype == PKV_F32) return fail(PKV_ERR_UNSUPPORTED, "chunk attention is built for float16 and bfloat16");
   if (num_seqs < 0) return fail(PKV_ERR_INVALID, "num_seqs %d < 0", num_seqs);
@@ -331,6 +336,7 @@ int pkv_paged_attn_chunk(void *out, const void *q, const void *k_pool, const voi
     return fail(PKV_ERR_INVALID, "too many work items");
   if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens || !query_start_loc)
     return fail(PKV_ERR_INVALID, "null array pointer");
+  if (fp8 && (!k_scale || !v_scale)) return fail(PKV_ERR_INVALID, "null scale pointer");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
     return fail(PKV_ERR_INVALID, "q, out, k_pool and v_pool must be 16-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -355,6 +361,8 @@ int pkv_paged_attn_chunk(void *out, const void *q, const void *k_pool, const voi
     a.block_shift = bshift;
     a.max_blocks = max_blocks_per_seq;
     a.num_blocks = num_blocks;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
     plan(block_size, max_blocks_per_seq, &a.partition_tokens, &a.max_parts);
     const int64_t items = (int64_t)num_seqs * n_kv_heads * row_blocks;
     if (items * a.max_parts > (int64_t)INT32_MAX) return fail(PKV_ERR_INVALID, "too many work items");
@@ -371,7 +379,7 @@ int pkv_paged_attn_chunk(void *out, const void *q, const void *k_pool, const voi
         if (rc != PKV_OK) return rc;
       }
     }
-    hipError_t e = pkv::launch_chunk_rows(static_cast<pkv::DType>(dtype), head_dim, false, a, st);
+    hipError_t e = pkv::launch_chunk_rows(static_cast<pkv::DType>(dtype), head_dim, fp8, a, st);
     if (e != hipSuccess) return hip_fail(e, "chunk attention launch");
     return ok();
   }
@@ -394,18 +402,49 @@ int pkv_paged_attn_chunk(void *out, const void *q, const void *k_pool, const voi
   a.num_blocks = num_blocks;
   a.row_blocks = (int32_t)(((int64_t)max_query_len * group + pkv::chunk_rows_per_block() - 1) /
                            pkv::chunk_rows_per_block());
-  hipError_t e = pkv::launch_chunk(static_cast<pkv::DType>(dtype), head_dim, a, st);
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  hipError_t e = pkv::launch_chunk(static_cast<pkv::DType>(dtype), head_dim, fp8, a, st);
   if (e != hipSuccess) return hip_fail(e, "chunk attention launch");
   return ok();
 }
 
-int pkv_paged_attn_decode_shared_prefix(void *out, const void *q, const void *k_pool, const void *v_pool,
-                                        const int32_t *block_tables, const int32_t *seq_lens,
-                                        const int32_t *prefix_lens, const int32_t *group_start, float scale,
-                                        int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
-                                        int32_t num_seqs, int32_t num_groups, int32_t max_group_size,
-                                        int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
-                                        void *stream) {
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_attn_chunk(void *out, const void *q, const void *k_pool, const void *v_pool,
+                         const int32_t *block_tables, const int32_t *seq_lens, const int32_t *query_start_loc,
+                         float scale, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t num_seqs, int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_query_len,
+                         int32_t dtype, void *stream) {
+  return chunk_impl(out, q, k_pool, v_pool, block_tables, seq_lens, query_start_loc, scale, n_heads, n_kv_heads,
+                    head_dim, block_size, num_seqs, max_blocks_per_seq, num_blocks, max_query_len, dtype, stream,
+                    false, nullptr, nullptr);
+}
+
+int pkv_paged_attn_chunk_fp8(void *out, const void *q, const void *k_pool, const void *v_pool,
+                             const float *k_scale, const float *v_scale, const int32_t *block_tables,
+                             const int32_t *seq_lens, const int32_t *query_start_loc, float scale, int32_t n_heads,
+                             int32_t n_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_seqs,
+                             int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_query_len, int32_t dtype,
+                             void *stream) {
+  return chunk_impl(out, q, k_pool, v_pool, block_tables, seq_lens, query_start_loc, scale, n_heads, n_kv_heads,
+                    head_dim, block_size, num_seqs, max_blocks_per_seq, num_blocks, max_query_len, dtype, stream,
+                    true, k_scale, v_scale);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared by the 16-bit and the FP8 shared-prefix entry points.
+int shared_prefix_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
+                       const int32_t *block_tables, const int32_t *seq_lens, const int32_t *prefix_lens,
+                       const int32_t *group_start, float scale, int32_t n_heads, int32_t n_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t num_seqs, int32_t num_groups,
+                       int32_t max_group_size, int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
+                       void *stream, bool fp8, const float *k_scale, const float *v_scale) {
   if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID, "unknown dtype %d", dtype);
   if (dtype == PKV_F32)
     return fail(PKV_ERR_UNSUPPORTED, "shared-prefix decode is built for float16 and bfloat16");
@@ -432,6 +471,7 @@ int pkv_paged_attn_decode_shared_prefix(void *out, const void *q, const void *k_
     return fail(PKV_ERR_INVALID, "max_group_size %d outside [1, num_seqs = %d]", max_group_size, num_seqs);
   if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens || !prefix_lens || !group_start)
     return fail(PKV_ERR_INVALID, "null array pointer");
+  if (fp8 && (!k_scale || !v_scale)) return fail(PKV_ERR_INVALID, "null scale pointer");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
     return fail(PKV_ERR_INVALID, "q, out, k_pool and v_pool must be 16-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -457,6 +497,8 @@ int pkv_paged_attn_decode_shared_prefix(void *out, const void *q, const void *k_
   suf.num_blocks = num_blocks;
   suf.prefix_lens = prefix_lens;
   suf.member_seqs = num_seqs;
+  suf.k_scale = k_scale;
+  suf.v_scale = v_scale;
   plan(block_size, max_blocks_per_seq, &suf.partition_tokens, &suf.max_parts);
 
   const int64_t max_tokens = (int64_t)max_blocks_per_seq * block_size;
@@ -498,7 +540,7 @@ int pkv_paged_attn_decode_shared_prefix(void *out, const void *q, const void *k_
       a.part_ml = reinterpret_cast<float2 *>(static_cast<char *>(ws) + acc_bytes);
       rc = get_arrivals(st, (int64_t)num_seqs * n_kv_heads, &a.arrivals);
       if (rc != PKV_OK) return rc;
-      hipError_t e = pkv::launch_shared_fused(static_cast<pkv::DType>(dtype), head_dim, a, st);
+      hipError_t e = pkv::launch_shared_fused(static_cast<pkv::DType>(dtype), head_dim, fp8, a, st);
       if (e != hipSuccess) return hip_fail(e, "shared-prefix decode launch");
       return ok();
     }
@@ -556,9 +598,38 @@ int pkv_paged_attn_decode_shared_prefix(void *out, const void *q, const void *k_
     if (pre_fused) pre.arrivals = arr;
     if (suf_fused) suf.arrivals = arr;
   }
-  hipError_t e = pkv::launch_shared_prefix(static_cast<pkv::DType>(dtype), head_dim, pre, suf, st);
+  hipError_t e = pkv::launch_shared_prefix(static_cast<pkv::DType>(dtype), head_dim, fp8, pre, suf, st);
   if (e != hipSuccess) return hip_fail(e, "shared-prefix decode launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_attn_decode_shared_prefix(void *out, const void *q, const void *k_pool, const void *v_pool,
+                                        const int32_t *block_tables, const int32_t *seq_lens,
+                                        const int32_t *prefix_lens, const int32_t *group_start, float scale,
+                                        int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                                        int32_t num_seqs, int32_t num_groups, int32_t max_group_size,
+                                        int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
+                                        void *stream) {
+  return shared_prefix_impl(out, q, k_pool, v_pool, block_tables, seq_lens, prefix_lens, group_start, scale,
+                            n_heads, n_kv_heads, head_dim, block_size, num_seqs, num_groups, max_group_size,
+                            max_blocks_per_seq, num_blocks, dtype, stream, false, nullptr, nullptr);
+}
+
+int pkv_paged_attn_decode_shared_prefix_fp8(void *out, const void *q, const void *k_pool, const void *v_pool,
+                                            const float *k_scale, const float *v_scale,
+                                            const int32_t *block_tables, const int32_t *seq_lens,
+                                            const int32_t *prefix_lens, const int32_t *group_start, float scale,
+                                            int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                                            int32_t block_size, int32_t num_seqs, int32_t num_groups,
+                                            int32_t max_group_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                                            int32_t dtype, void *stream) {
+  return shared_prefix_impl(out, q, k_pool, v_pool, block_tables, seq_lens, prefix_lens, group_start, scale,
+                            n_heads, n_kv_heads, head_dim, block_size, num_seqs, num_groups, max_group_size,
+                            max_blocks_per_seq, num_blocks, dtype, stream, true, k_scale, v_scale);
 }
 
 int pkv_kv_cache_write_fp8(void *k_pool, void *v_pool, const void *k_new, const void *v_new,

@@ -49,11 +49,13 @@ constexpr int kPfRowsPerWave = 32;
 constexpr int kPfRows = kPfWaves * kPfRowsPerWave;  // 256 query rows per workgroup
 constexpr int kPfStage = 64;                         // context tokens per stage
 
-template <typename T, int D> struct PfCfg {
-  static constexpr int kCh = D / 8;                                // 16-byte chunks per token row
+template <typename T, int D, bool F8> struct PfCfg {
+  static constexpr int kCh = D / 8;                                // 16-byte chunks per token row (in LDS)
+  static constexpr int kChKV = F8 ? D / 16 : D / 8;                // 16-byte chunks per stored token row
+  static constexpr int kTileChunks = kPfStage * kChKV;             // 16-byte chunks of one stored tile
   static constexpr int kSteps = kCh / 4;                           // QK MFMA steps (32 dims each)
   static constexpr int kDimBlocks = D / 16;                        // 16-dim output blocks
-  static constexpr int kLoads = kPfStage * kCh / (kPfWaves * 64);  // 16-byte loads per thread per tile
+  static constexpr int kLoads = (kTileChunks + kPfWaves * 64 - 1) / (kPfWaves * 64);  // per thread per tile
   static constexpr int kTileBytes = kPfStage * kCh * 16;           // one K (or V) stage in LDS
   static constexpr int kBufBytes = 2 * kTileBytes;                 // K + V
   static constexpr int kSmem = 2 * kBufBytes;                      // double buffer
@@ -68,10 +70,15 @@ template <typename T> __device__ __forceinline__ uint32_t pack2(float a, float b
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{a, b}), t2));
 }
 
-template <typename T, int D>
+// F8: the pools hold OCP e4m3 codes with one scale per KV head; each 16-byte
+// load (16 codes of one token) is decoded exactly into two 16-byte chunks of T
+// on its way into LDS, k_scale is folded into the score scale and v_scale
+// into the output.
+template <typename T, int D, bool F8>
 __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void paged_chunk_kernel(ChunkArgs a) {
-  using C = PfCfg<T, D>;
+  using C = PfCfg<T, D, F8>;
+  constexpr int kChKV = C::kChKV;
   constexpr int kCh = C::kCh;
   constexpr int kL = C::kLoads;
   constexpr int kDB = C::kDimBlocks;
@@ -153,8 +160,8 @@ void paged_chunk_kernel(ChunkArgs a) {
     u32x4_t k[kL];
     u32x4_t v[kL];
   };
-  // loads of stage st into registers: thread chunk u = tid + 256 i is chunk
-  // u % kCh of token u / kCh; tokens at or past ctx_end stay zero
+  // loads of stage st into registers: thread chunk u = tid + 512 i is stored
+  // chunk u % kChKV of token u / kChKV; tokens at or past ctx_end stay zero
   auto load_stage = [&](int st, Regs &rg) {
     const int t0 = st * kPfStage;
     const int last_blk = (min(t0 + kPfStage, ctx_end) - 1) >> a.block_shift;
@@ -165,17 +172,17 @@ void paged_chunk_kernel(ChunkArgs a) {
 #pragma unroll
     for (int i = 0; i < kL; ++i) {
       const int u = tid + i * kPfWaves * 64;
-      const int tok = t0 + u / kCh;
+      const int tok = t0 + u / kChKV;
       rg.k[i] = rg.v[i] = u32x4_t{0u, 0u, 0u, 0u};
       const int j = (min(tok, ctx_end - 1) >> a.block_shift) - win;  // 0 .. 63
       int phys = __shfl(btv, j, 64);
-      if (tok < ctx_end) {
+      if (tok < ctx_end && u < C::kTileChunks) {
         if (phys < 0 || (int64_t)phys >= a.num_blocks) {
           bad = true;
           phys = 0;
         }
         const int64_t off = ((int64_t)phys * kv_stride_blk + (int64_t)g * a.block_size +
-                             (tok & (a.block_size - 1))) * kCh + u % kCh;
+                             (tok & (a.block_size - 1))) * kChKV + u % kChKV;
         rg.k[i] = __builtin_nontemporal_load(kbase + off);
         rg.v[i] = __builtin_nontemporal_load(vbase + off);
       }
@@ -187,10 +194,21 @@ void paged_chunk_kernel(ChunkArgs a) {
 #pragma unroll
     for (int i = 0; i < kL; ++i) {
       const int u = tid + i * kPfWaves * 64;
-      const int tr = u / kCh;
-      const int ch = u % kCh;
-      ks[kst_slot<kCh>(tr, ch)] = rg.k[i];
-      vs[tr * kCh + (ch ^ vst_swz<kCh>(tr))] = rg.v[i];
+      if (u >= C::kTileChunks) continue;
+      const int tr = u / kChKV;
+      const int ch = u % kChKV;
+      if constexpr (F8) {
+        u32x4_t lo, hi;
+        fp8x16_to<T>(rg.k[i], lo, hi);
+        ks[kst_slot<kCh>(tr, 2 * ch)] = lo;
+        ks[kst_slot<kCh>(tr, 2 * ch + 1)] = hi;
+        fp8x16_to<T>(rg.v[i], lo, hi);
+        vs[tr * kCh + ((2 * ch) ^ vst_swz<kCh>(tr))] = lo;
+        vs[tr * kCh + ((2 * ch + 1) ^ vst_swz<kCh>(tr))] = hi;
+      } else {
+        ks[kst_slot<kCh>(tr, ch)] = rg.k[i];
+        vs[tr * kCh + (ch ^ vst_swz<kCh>(tr))] = rg.v[i];
+      }
     }
   };
 
@@ -207,7 +225,12 @@ void paged_chunk_kernel(ChunkArgs a) {
 #pragma unroll
     for (int b = 0; b < kDB; ++b) acc[rt][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   constexpr float kLazy = 8.f;
-  const float sl2 = a.scale_log2;
+  float sl2 = a.scale_log2;  // scores in base-2 units
+  float vsc = 1.f;           // output scale
+  if constexpr (F8) {
+    sl2 *= a.k_scale[g];
+    vsc = a.v_scale[g];
+  }
   // transposed V reads: this lane addresses token 4 kg + (n >> 2) of a 16-token block
   const int tr_tok = 4 * kg + (n >> 2);
   const int v_tr_off = tr_tok * kCh * 16 + (lane & 3) * 8;
@@ -317,7 +340,7 @@ void paged_chunk_kernel(ChunkArgs a) {
   const int any_bad = __syncthreads_or(bad ? 1 : 0);
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    const float inv = 1.f / lsum[rt][0];
+    const float inv = vsc / lsum[rt][0];
     if (!rvalid[rt]) continue;
     T *orow = out + out_row(wrow0 + 16 * rt + n) * D;
 #pragma unroll
@@ -331,21 +354,21 @@ void paged_chunk_kernel(ChunkArgs a) {
   }
 }
 
-template <typename T, int D> hipError_t launch_chunk_td(const ChunkArgs &a, hipStream_t stream) {
-  constexpr int kSmem = PfCfg<T, D>::kSmem;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&paged_chunk_kernel<T, D>),
+template <typename T, int D, bool F8> hipError_t launch_chunk_td(const ChunkArgs &a, hipStream_t stream) {
+  constexpr int kSmem = PfCfg<T, D, F8>::kSmem;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&paged_chunk_kernel<T, D, F8>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, kSmem);
   if (attr != hipSuccess) return attr;
   const dim3 grid((unsigned)((int64_t)a.n_kv_heads * a.num_seqs * a.row_blocks));
-  hipLaunchKernelGGL((paged_chunk_kernel<T, D>), grid, dim3(kPfWaves * 64), kSmem, stream, a);
+  hipLaunchKernelGGL((paged_chunk_kernel<T, D, F8>), grid, dim3(kPfWaves * 64), kSmem, stream, a);
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool F8>
 hipError_t launch_chunk_t(int head_dim, const ChunkArgs &a, hipStream_t stream) {
   switch (head_dim) {
-    case 64: return launch_chunk_td<T, 64>(a, stream);
-    case 128: return launch_chunk_td<T, 128>(a, stream);
+    case 64: return launch_chunk_td<T, 64, F8>(a, stream);
+    case 128: return launch_chunk_td<T, 128, F8>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -354,10 +377,12 @@ hipError_t launch_chunk_t(int head_dim, const ChunkArgs &a, hipStream_t stream) 
 
 int chunk_rows_per_block() { return kPfRows; }
 
-hipError_t launch_chunk(DType dt, int head_dim, const ChunkArgs &a, hipStream_t stream) {
+hipError_t launch_chunk(DType dt, int head_dim, bool fp8, const ChunkArgs &a, hipStream_t stream) {
   switch (dt) {
-    case DType::F16: return launch_chunk_t<_Float16>(head_dim, a, stream);
-    case DType::BF16: return launch_chunk_t<__bf16>(head_dim, a, stream);
+    case DType::F16: return fp8 ? launch_chunk_t<_Float16, true>(head_dim, a, stream)
+                                : launch_chunk_t<_Float16, false>(head_dim, a, stream);
+    case DType::BF16: return fp8 ? launch_chunk_t<__bf16, true>(head_dim, a, stream)
+                                 : launch_chunk_t<__bf16, false>(head_dim, a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1418,53 +1418,57 @@ hipError_t launch_chunk_rows(DType dt, int head_dim, bool fp8, const DecodeArgs 
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool F8>
 hipError_t launch_shared_prefix_td(int gt, const DecodeArgs &pre, const DecodeArgs &suf, hipStream_t stream) {
-  hipError_t e = launch_t<T, D, 16, false, kModePrefix>(pre, stream);
+  hipError_t e = launch_t<T, D, 16, F8, kModePrefix>(pre, stream);
   if (e != hipSuccess) return e;
   switch (gt) {
-    case 1: return launch_t<T, D, 1, false, kModeSuffix>(suf, stream);
-    case 2: return launch_t<T, D, 2, false, kModeSuffix>(suf, stream);
-    case 4: return launch_t<T, D, 4, false, kModeSuffix>(suf, stream);
-    case 8: return launch_t<T, D, 8, false, kModeSuffix>(suf, stream);
-    case 16: return launch_t<T, D, 16, false, kModeSuffix>(suf, stream);
+    case 1: return launch_t<T, D, 1, F8, kModeSuffix>(suf, stream);
+    case 2: return launch_t<T, D, 2, F8, kModeSuffix>(suf, stream);
+    case 4: return launch_t<T, D, 4, F8, kModeSuffix>(suf, stream);
+    case 8: return launch_t<T, D, 8, F8, kModeSuffix>(suf, stream);
+    case 16: return launch_t<T, D, 16, F8, kModeSuffix>(suf, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename T>
+template <typename T, bool F8>
 hipError_t launch_shared_fused_t(int head_dim, const DecodeArgs &a, hipStream_t stream) {
   switch (head_dim) {
-    case 64: return launch_t<T, 64, 16, false, kModeShared>(a, stream);
-    case 128: return launch_t<T, 128, 16, false, kModeShared>(a, stream);
+    case 64: return launch_t<T, 64, 16, F8, kModeShared>(a, stream);
+    case 128: return launch_t<T, 128, 16, F8, kModeShared>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename T>
+template <typename T, bool F8>
 hipError_t launch_shared_prefix_t(int head_dim, int gt, const DecodeArgs &pre, const DecodeArgs &suf,
                                   hipStream_t stream) {
   switch (head_dim) {
-    case 64: return launch_shared_prefix_td<T, 64>(gt, pre, suf, stream);
-    case 128: return launch_shared_prefix_td<T, 128>(gt, pre, suf, stream);
+    case 64: return launch_shared_prefix_td<T, 64, F8>(gt, pre, suf, stream);
+    case 128: return launch_shared_prefix_td<T, 128, F8>(gt, pre, suf, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_shared_prefix(DType dt, int head_dim, const DecodeArgs &pre, const DecodeArgs &suf,
+hipError_t launch_shared_prefix(DType dt, int head_dim, bool fp8, const DecodeArgs &pre, const DecodeArgs &suf,
                                 hipStream_t stream) {
   const int gt = decode_head_tile(suf.group);
   switch (dt) {
-    case DType::F16: return launch_shared_prefix_t<_Float16>(head_dim, gt, pre, suf, stream);
-    case DType::BF16: return launch_shared_prefix_t<__bf16>(head_dim, gt, pre, suf, stream);
+    case DType::F16: return fp8 ? launch_shared_prefix_t<_Float16, true>(head_dim, gt, pre, suf, stream)
+                                : launch_shared_prefix_t<_Float16, false>(head_dim, gt, pre, suf, stream);
+    case DType::BF16: return fp8 ? launch_shared_prefix_t<__bf16, true>(head_dim, gt, pre, suf, stream)
+                                 : launch_shared_prefix_t<__bf16, false>(head_dim, gt, pre, suf, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_shared_fused(DType dt, int head_dim, const DecodeArgs &a, hipStream_t stream) {
+hipError_t launch_shared_fused(DType dt, int head_dim, bool fp8, const DecodeArgs &a, hipStream_t stream) {
   switch (dt) {
-    case DType::F16: return launch_shared_fused_t<_Float16>(head_dim, a, stream);
-    case DType::BF16: return launch_shared_fused_t<__bf16>(head_dim, a, stream);
+    case DType::F16: return fp8 ? launch_shared_fused_t<_Float16, true>(head_dim, a, stream)
+                                : launch_shared_fused_t<_Float16, false>(head_dim, a, stream);
+    case DType::BF16: return fp8 ? launch_shared_fused_t<__bf16, true>(head_dim, a, stream)
+                                 : launch_shared_fused_t<__bf16, false>(head_dim, a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -105,12 +105,16 @@ struct ChunkArgs {
   int32_t max_blocks;
   int64_t num_blocks;
   int32_t row_blocks;              // ceil(max_query_len * group / chunk_rows_per_block())
+  // FP8 (e4m3) pools only (launch_chunk with fp8): per-KV-head scales
+  const float *k_scale;
+  const float *v_scale;
 };
 
 // Query rows (chunk token x query head pairs) per chunk-kernel workgroup.
 int chunk_rows_per_block();
 
-hipError_t launch_chunk(DType dt, int head_dim, const ChunkArgs &a, hipStream_t stream);
+// fp8: pools of e4m3 codes with a.k_scale / a.v_scale; dt (q, out) F16 or BF16.
+hipError_t launch_chunk(DType dt, int head_dim, bool fp8, const ChunkArgs &a, hipStream_t stream);
 
 // Chunk attention on the decode kernel's work items (16 rows of (token, head)
 // pairs per item, split along the sequence and merged like decode); dt is
@@ -120,14 +124,15 @@ hipError_t launch_chunk_rows(DType dt, int head_dim, bool fp8, const DecodeArgs 
 // Shared-prefix decode: the prefix launch (pre: rows mode over groups, head
 // tile 16) then the suffix launch (suf: decode of the private tokens with the
 // prefix partials folded in); dt is F16 or BF16.
-hipError_t launch_shared_prefix(DType dt, int head_dim, const DecodeArgs &pre, const DecodeArgs &suf,
+hipError_t launch_shared_prefix(DType dt, int head_dim, bool fp8, const DecodeArgs &pre, const DecodeArgs &suf,
                                 hipStream_t stream);
 
 // Shared-prefix decode in one launch: prefix and private partitions are work
 // items of one grid, merged per (sequence, KV head) by the last to finish.
 // Needs n_heads / n_kv_heads in {1, 2, 4, 8, 16} and every group's members x
-// heads per KV head <= 16; dt is F16 or BF16.
-hipError_t launch_shared_fused(DType dt, int head_dim, const DecodeArgs &a, hipStream_t stream);
+// heads per KV head <= 16; dt is F16 or BF16; fp8 selects e4m3 pools with
+// a.k_scale / a.v_scale (also for launch_shared_prefix).
+hipError_t launch_shared_fused(DType dt, int head_dim, bool fp8, const DecodeArgs &a, hipStream_t stream);
 
 // Same over FP8 (OCP e4m3) pools with a.k_scale / a.v_scale; dt (query and
 // output) must be F16 or BF16.

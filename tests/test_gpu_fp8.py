@@ -34,16 +34,19 @@ def say(msg):
     sys.stdout.flush()
 
 
-def head_scales(x, n_kv_heads):
-    """Per-head scale amax / 448 of float rows ``[..., Hkv, D]`` (any positive scale is valid)."""
-    a = np.abs(f32np(x)).reshape(-1, n_kv_heads, x.shape[-1]).max(axis=(0, 2))
+def head_scales(pool, n_kv_heads):
+    """Per-KV-head scale amax / 448 of a pool ``[NB, Hkv, BS, D]``, so that every
+    stored value fits e4m3 (any positive scale is valid; this one saturates nothing)."""
+    a = np.abs(f32np(pool))
+    a = np.moveaxis(a, 1, 0).reshape(n_kv_heads, -1).max(axis=1)
     return np.maximum(a / 448.0, 1e-6).astype(np.float32)
 
 
 def fp8_case(w, seed):
     """FP8 pools of a workload: its float pools divided by per-head scales and
     converted to e4m3 codes by torch (input generation only: both sides then
-    read the same codes); unreferenced slots keep the poison NaN code."""
+    read the same codes); unreferenced slots keep the poison NaN code, every
+    referenced slot holds a finite code."""
     ks = head_scales(w.k_pool.nan_to_num(0.0), w.n_kv_heads)
     vs = head_scales(w.v_pool.nan_to_num(0.0), w.n_kv_heads)
 
@@ -51,7 +54,14 @@ def fp8_case(w, seed):
         x = pool.float() / torch.from_numpy(scale)[None, :, None, None]
         return x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
-    return codes(w.k_pool, ks), codes(w.v_pool, vs), ks, vs
+    kc, vc = codes(w.k_pool, ks), codes(w.v_pool, vs)
+    # NaN codes (S.1111.111) only in the poison: none in any sequence's tokens
+    for s_, L in enumerate(w.seq_lens):
+        j = np.arange(int(L))
+        blk, off = w.block_tables[s_, j // w.block_size], j % w.block_size
+        for c in (kc, vc):
+            assert not np.any((c[blk, :, off] & 0x7F) == 0x7F), "NaN code inside a sequence"
+    return kc, vc, ks, vs
 
 
 def gpu_decode_fp8(w, kc, vc, ks, vs, seq_lens=None):
@@ -163,3 +173,76 @@ def test_fp8_copy_blocks_bit_exact():
     from oracle.block_manager import copy_blocks
     k_ref, v_ref = copy_blocks(k, v, pairs)
     assert np.array_equal(kd.cpu().numpy(), k_ref) and np.array_equal(vd.cpu().numpy(), v_ref)
+
+
+def dequant_f64(codes, scale):
+    """float64 pool of the dequantized codes (decode(code) * scale per KV head)."""
+    return ofp8.dequantize_pool(codes, scale)
+
+
+@pytest.mark.parametrize("qmax,H,Hkv,D,BS,dtype", [(4, 32, 8, 128, 16, torch.bfloat16),
+                                                   (300, 32, 8, 128, 16, torch.bfloat16),
+                                                   (200, 8, 8, 64, 32, torch.float16)])
+def test_fp8_chunk(qmax, H, Hkv, D, BS, dtype):
+    """Chunk attention over FP8 pools: short chunks (decode-kernel rows) and
+    prefill chunks (the prefill kernel), against the oracle on the
+    dequantized pools."""
+    import oracle
+    say(f"fp8 chunk qmax={qmax} H={H} Hkv={Hkv} D={D}")
+    w = workloads.random_case(90 + qmax + D, num_seqs=5, n_heads=H, n_kv_heads=Hkv, head_dim=D, block_size=BS,
+                              dtype=dtype, max_len=2200, min_len=400, poison=True)
+    kc, vc, ks, vs = fp8_case(w, 0)
+    rng = np.random.default_rng(qmax)
+    qlens = np.minimum(rng.integers(1, qmax + 1, size=w.num_seqs), w.seq_lens)
+    qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    g = torch.Generator().manual_seed(qmax)
+    q = torch.randn(int(qsl[-1]), H, D, generator=g).to(dtype)
+    dev = "cuda"
+    out = torch.empty(q.shape, dtype=dtype, device=dev)
+    _lib.paged_attn_chunk_fp8(out, q.to(dev), torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev),
+                              torch.from_numpy(ks).to(dev), torch.from_numpy(vs).to(dev),
+                              torch.from_numpy(w.block_tables).to(dev), torch.from_numpy(w.seq_lens).to(dev),
+                              torch.from_numpy(qsl).to(dev), w.scale, H, Hkv, D, BS, int(qlens.max()))
+    torch.cuda.synchronize()
+    G = H // Hkv
+    ref = np.zeros(tuple(q.shape))
+    qn = f32np(q)
+    for kv in range(Hkv):
+        ref[:, kv * G:(kv + 1) * G] = oracle.paged_attn_chunk(
+            qn[:, kv * G:(kv + 1) * G], dequant_f64(kc[:, kv:kv + 1], ks[kv:kv + 1]),
+            dequant_f64(vc[:, kv:kv + 1], vs[kv:kv + 1]), w.block_tables, w.seq_lens, qsl, w.scale, G, 1, D, BS)
+    err = max_abs_err(out, ref)
+    say(f"  max abs err {err:.3e}")
+    assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("case", ["prompt_samples", "three_heads_per_kv"])
+def test_fp8_shared_prefix(case):
+    """Shared-prefix decode over FP8 pools: the 16-prompt x 4-sample workload
+    (one launch) and 3 query heads per KV head (prefix and private launches)."""
+    if case == "prompt_samples":
+        w = workloads.make(5, poison=True)
+        gs, pl, mg = _lib.shared_prefix_groups(w.block_tables, w.seq_lens, w.block_size)
+    else:
+        rng = np.random.default_rng(4)
+        sizes, pblk = [3, 1, 4], [6, 0, 11]
+        w = workloads.build_groups(name="g3", rng=rng, group_sizes=sizes, prefix_blocks=pblk,
+                                   private_lens=rng.integers(0, 300, size=8), n_heads=12, n_kv_heads=4,
+                                   head_dim=128, block_size=16, dtype=torch.bfloat16, poison=True)
+        gs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+        pl = np.repeat(np.asarray(pblk) * 16, sizes).astype(np.int32)
+        mg = max(sizes)
+    say(f"fp8 shared prefix {case}")
+    kc, vc, ks, vs = fp8_case(w, 0)
+    dev = "cuda"
+    q = w.q.to(dev)
+    out = torch.empty_like(q)
+    _lib.paged_attn_decode_shared_prefix_fp8(
+        out, q, torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev), torch.from_numpy(ks).to(dev),
+        torch.from_numpy(vs).to(dev), torch.from_numpy(w.block_tables).to(dev), torch.from_numpy(w.seq_lens).to(dev),
+        torch.from_numpy(np.asarray(pl, np.int32)).to(dev), torch.from_numpy(np.asarray(gs, np.int32)).to(dev),
+        w.scale, w.n_heads, w.n_kv_heads, w.head_dim, w.block_size, int(mg))
+    torch.cuda.synchronize()
+    err = max_abs_err(out, oracle_fp8(w, kc, vc, ks, vs))
+    say(f"  max abs err {err:.3e}")
+    assert err <= TOL[w.dtype]
