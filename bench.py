@@ -44,10 +44,11 @@ PROFILE_NAMES = {1: "paged_decode_tiny_f32_b4", 2: "paged_decode_mha_bf16_b64",
                  5: "paged_decode_prefix_f16_b64"}
 
 
-def measured_traffic(cfg):
-    """HBM bytes per decode call from the committed counter summary, or None when
-    there is none or the decode source changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", PROFILE_NAMES[cfg] + "_traffic.json")
+def measured_traffic(cfg, fused=True):
+    """HBM bytes per timed call from the committed counter summary of that step,
+    or None when there is none or the decode source changed since the counters
+    were taken."""
+    path = os.path.join(ROOT, "profiles", PROFILE_NAMES[cfg] + ("" if fused else "_two_call") + "_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -299,6 +300,9 @@ def main():
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "chunk", "shared_prefix"],
                     help="decode = the hot-path step (default); copy_blocks = copy-on-write block copy")
+    ap.add_argument("--step", default="append", choices=["append", "two-call"],
+                    help="decode step: one call that appends the new token and decodes (default), or the "
+                         "cache write followed by the decode call (always so for FP8 pools)")
     ap.add_argument("--kv", default="native", choices=["native", "fp8"],
                     help="KV pool storage: the query dtype (default) or FP8 e4m3 codes with per-head scales")
     args = ap.parse_args()
@@ -361,7 +365,19 @@ def main():
         vps.append(vps[0].clone())
     stream = torch.cuda.current_stream(dev)
 
+    # 16-bit pools: one call appends the new token and decodes (the fused
+    # step); --step two-call (and FP8 pools) time the write kernel, then decode
+    fused = args.step == "append" and not fp8
+
     def step(r, ev=None):
+        if fused:
+            if ev is not None:
+                ev[0].record(stream)
+            _lib.paged_attn_decode_append(out, q, kps[r], vps[r], kn, vn, bt, sl, w.scale, w.n_heads,
+                                          w.n_kv_heads, w.head_dim, w.block_size, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+            return
         if fp8:
             _lib.kv_cache_write_fp8(kps[r], vps[r], kn, vn, ksd, vsd, slots, stream=stream)
         else:
@@ -402,11 +418,15 @@ def main():
     dec_bytes = (accounting.decode_kv_bytes(lens1, w.n_kv_heads, w.head_dim, e_kv)
                  + accounting.decode_qo_bytes(w.num_seqs, w.n_heads, w.head_dim, e))
     n_written = int((w.slot_mapping >= 0).sum())
-    wr_bytes = 2 * n_written * w.n_kv_heads * w.head_dim * (e + e_kv)  # read new rows, write pool rows
-    step_bytes = dec_bytes + wr_bytes
+    # the step's compulsory bytes: decode at the new lengths (which reads each
+    # new K/V row once) plus the new rows stored into the pools
+    store_bytes = 2 * n_written * w.n_kv_heads * w.head_dim * e_kv
+    step_bytes = dec_bytes + store_bytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
     dec_mean = float(dec_ms.mean())
-    achieved = dec_bytes / (dec_mean * 1e-3) / 1e9
+    # the timed call: the whole step when fused, else the decode call alone
+    call_bytes = step_bytes if fused else dec_bytes
+    achieved = call_bytes / (dec_mean * 1e-3) / 1e9
     ptok, nparts = _lib.decode_plan(w.n_heads, w.n_kv_heads, w.block_size, w.num_seqs,
                                     w.max_blocks_per_seq)
 
@@ -430,23 +450,25 @@ def main():
             "cached_tokens": int(lens1.sum()), "mean_seq_len": round(float(lens1.mean()), 1),
             "max_seq_len": int(lens1.max()), "num_blocks": w.num_blocks,
             "partition_tokens": ptok, "max_partitions": nparts, "pool_replicas": R,
-            "step": "kv_cache_write (1 token/seq) + paged_attn_decode (seq_len+1)",
+            "step": ("paged_attn_decode_append: one call writes the new token (1 per seq) and decodes seq_len+1"
+                     if fused else "kv_cache_write (1 token/seq) + paged_attn_decode (seq_len+1)"),
         },
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "us_per_batch": round(ms_step * 1e3, 3),
-        "decode_us": {"mean": round(dec_mean * 1e3, 3),
+        ("call_us" if fused else "decode_us"): {"mean": round(dec_mean * 1e3, 3),
                       "p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 3),
                       "p50": round(float(np.percentile(dec_ms, 50)) * 1e3, 3),
                       "p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 3)},
         "step_bytes": int(step_bytes),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None if fp8 else measured_traffic(args.config),
-                     "kernel": "paged_attn_decode call (decode kernel"
+                     "traffic": None if fp8 else measured_traffic(args.config, fused),
+                     "kernel": ("paged_attn_decode_append" if fused else "paged_attn_decode")
+                               + " call (decode kernel"
                                + (")" if nparts == 1 else
                                   ", partitions merged in-kernel)" if nparts <= FUSED_MERGE_PARTS else
                                   " + partition merge kernel)"),
-                     "algorithmic_bytes": int(dec_bytes)},
+                     "algorithmic_bytes": int(call_bytes)},
         "wall_ms_per_step": round(wall * 1e3 / K, 5),
     }
     if not args.no_ceiling:

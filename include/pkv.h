@@ -145,6 +145,33 @@ PKV_API int pkv_kv_cache_write(void *k_pool, void *v_pool, const void *k_new, co
                        int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t dtype,
                        void *stream);
 
+/*
+ * One decode step in one call: append each sequence's newest token, then
+ * attend. Equivalent to pkv_kv_cache_write of k_new / v_new into the slots
+ * of positions seq_lens[s] - 1 (slot = block_tables[s, (L - 1) / block_size] *
+ * block_size + (L - 1) % block_size) followed by pkv_paged_attn_decode with
+ * seq_lens, which here count the new token. The vLLM notes page's engine
+ * step (allocate the slots, then run the forward pass that writes the new
+ * K/V and attends) is the sequence these two calls follow; one kernel does
+ * both: the work item that holds a sequence's newest token writes it to the
+ * pool and uses it from on-chip memory instead of reading it back, which
+ * removes the separate write kernel and its launch from every step.
+ *
+ * Arguments: as in pkv_paged_attn_decode, plus
+ *   k_pool, v_pool  read and written (the new rows are stored)
+ *   k_new, v_new    read, [num_seqs, n_kv_heads, head_dim] of dtype, 16-byte aligned
+ *   seq_lens        read, tokens per sequence including the new one (>= 1; 0 =
+ *                   empty sequence: zero output, nothing written)
+ *   dtype           PKV_F16 or PKV_BF16 (PKV_F32 gives PKV_ERR_UNSUPPORTED)
+ * Device-side checks as in pkv_paged_attn_decode; a sequence with an invalid
+ * length or table entry gets NaN rows and no write.
+ */
+PKV_API int pkv_paged_attn_decode_append(void *out, const void *q, void *k_pool, void *v_pool, const void *k_new,
+                                         const void *v_new, const int32_t *block_tables, const int32_t *seq_lens,
+                                         float scale, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                                         int32_t block_size, int32_t num_seqs, int32_t max_blocks_per_seq,
+                                         int64_t num_blocks, int32_t dtype, void *stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 PKV_API const char *pkv_last_error(void);
 

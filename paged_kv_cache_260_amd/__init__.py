@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     paged_attn_chunk,
     paged_attn_chunk_fp8,
     paged_attn_decode,
+    paged_attn_decode_append,
     paged_attn_decode_fp8,
     paged_attn_decode_shared_prefix,
     paged_attn_decode_shared_prefix_fp8,
@@ -34,6 +35,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "paged_attn_decode",
+    "paged_attn_decode_append",
     "BlockManager",
     "copy_blocks",
     "paged_attn_decode_fp8",

@@ -66,6 +66,15 @@ def write_bytes(num_written: int, n_kv_heads: int, head_dim: int, elem_bytes: in
     return 4 * num_written * n_kv_heads * head_dim * elem_bytes
 
 
+def decode_append_bytes(seq_lens_after, num_written, n_heads, n_kv_heads, head_dim, elem_bytes) -> int:
+    """Compulsory bytes of one decode step that appends each sequence's new
+    token and attends over all ``L + 1`` tokens: the decode bytes at the new
+    lengths (the new K/V rows are read once, as part of them) plus the new rows
+    stored into the pools (``2 * n * Hkv * D * e``)."""
+    return (decode_compulsory_bytes(seq_lens_after, n_heads, n_kv_heads, head_dim, elem_bytes)
+            + 2 * num_written * n_kv_heads * head_dim * elem_bytes)
+
+
 def utilisation(seq_lens, block_size: int) -> float:
     """Share of allocated block slots that hold a cached token: ``sum L / (sum ceil(L/BS) * BS)``."""
     lens = np.asarray(seq_lens, dtype=np.int64)

@@ -204,10 +204,14 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
                 const int32_t *block_tables, const int32_t *seq_lens, float scale, int32_t n_heads,
                 int32_t n_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_seqs,
                 int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype, void *stream, bool fp8,
-                const float *k_scale, const float *v_scale) {
+                const float *k_scale, const float *v_scale, const void *k_new = nullptr,
+                const void *v_new = nullptr) {
   if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID, "unknown dtype %d", dtype);
   if (fp8 && dtype == PKV_F32)
     return fail(PKV_ERR_UNSUPPORTED, "FP8 pools need a float16 or bfloat16 query and output");
+  const bool append = k_new != nullptr || v_new != nullptr;
+  if (append && dtype == PKV_F32)
+    return fail(PKV_ERR_UNSUPPORTED, "decode with append is built for float16 and bfloat16");
   if (num_seqs < 0 || num_seqs > 65535)
     return fail(PKV_ERR_INVALID, "num_seqs %d outside [0, 65535]", num_seqs);
   if (n_heads < 1 || n_kv_heads < 1)
@@ -232,8 +236,11 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
   if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens)
     return fail(PKV_ERR_INVALID, "null array pointer");
   if (fp8 && (!k_scale || !v_scale)) return fail(PKV_ERR_INVALID, "null scale pointer");
+  if (append && (!k_new || !v_new)) return fail(PKV_ERR_INVALID, "null k_new or v_new");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
     return fail(PKV_ERR_INVALID, "q, out, k_pool and v_pool must be 16-byte aligned");
+  if (append && (!aligned16(k_new) || !aligned16(v_new)))
+    return fail(PKV_ERR_INVALID, "k_new and v_new must be 16-byte aligned");
 
   pkv::DecodeArgs a{};
   a.out = out;
@@ -255,6 +262,8 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
   a.num_blocks = num_blocks;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
+  a.k_new = k_new;
+  a.v_new = v_new;
   plan(block_size, max_blocks_per_seq, &a.partition_tokens, &a.max_parts);
   if ((int64_t)num_seqs * a.max_parts * n_kv_heads * a.head_chunks > (int64_t)INT32_MAX)
     return fail(PKV_ERR_INVALID, "%d sequences x %d partitions x %d heads: too many workgroups",
@@ -273,8 +282,9 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
       if (rc != PKV_OK) return rc;
     }
   }
-  hipError_t e = fp8 ? pkv::launch_decode_fp8(static_cast<pkv::DType>(dtype), head_dim, a, st)
-                     : pkv::launch_decode(static_cast<pkv::DType>(dtype), head_dim, a, st);
+  hipError_t e = append ? pkv::launch_decode_append(static_cast<pkv::DType>(dtype), head_dim, a, st)
+                 : fp8  ? pkv::launch_decode_fp8(static_cast<pkv::DType>(dtype), head_dim, a, st)
+                        : pkv::launch_decode(static_cast<pkv::DType>(dtype), head_dim, a, st);
   if (e != hipSuccess) return hip_fail(e, "paged decode launch");
   return ok();
 }
@@ -291,6 +301,16 @@ int pkv_paged_attn_decode(void *out, const void *q, const void *k_pool, const vo
   return decode_impl(out, q, k_pool, v_pool, block_tables, seq_lens, scale, n_heads, n_kv_heads, head_dim,
                      block_size, num_seqs, max_blocks_per_seq, num_blocks, dtype, stream, false, nullptr,
                      nullptr);
+}
+
+int pkv_paged_attn_decode_append(void *out, const void *q, void *k_pool, void *v_pool, const void *k_new,
+                                 const void *v_new, const int32_t *block_tables, const int32_t *seq_lens,
+                                 float scale, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t num_seqs, int32_t max_blocks_per_seq,
+                                 int64_t num_blocks, int32_t dtype, void *stream) {
+  return decode_impl(out, q, k_pool, v_pool, block_tables, seq_lens, scale, n_heads, n_kv_heads, head_dim,
+                     block_size, num_seqs, max_blocks_per_seq, num_blocks, dtype, stream, false, nullptr, nullptr,
+                     k_new, v_new);
 }
 
 int pkv_paged_attn_decode_fp8(void *out, const void *q, const void *k_pool, const void *v_pool,

@@ -80,7 +80,9 @@ template <typename T, int D, int GT> struct Cfg {
   // four waves as the MFMA A operand; rows GT..15 of the operand are zero
   static constexpr int kQOff = (kMemOff + 48 * 4 + 15) / 16 * 16;
   static constexpr int kQChunks = GT * kCh;
-  static constexpr int kSmem = kQOff + kQChunks * 16;
+  // append mode: the newest token's K and V rows (2 kCh chunks)
+  static constexpr int kNewOff = kQOff + kQChunks * 16;
+  static constexpr int kSmem = kNewOff + 2 * kCh * 16;
   static_assert(kCh % 4 == 0 && 64 % kCh == 0, "head_dim must give 8, 16 or 32 chunks");
   static_assert(!kPvMfma || kCh == 8 || kCh == 16, "MFMA P*V path: 8 or 16 chunks per row");
   static_assert(GT >= 1 && GT <= 16, "head tile");
@@ -104,6 +106,7 @@ constexpr int kModeChunk = 1;
 constexpr int kModePrefix = 2;
 constexpr int kModeSuffix = 3;
 constexpr int kModeShared = 4;
+constexpr int kModeAppend = 5;
 constexpr int kCompactChunks = kCompactSeqs / 64;
 constexpr int kRemBuckets = 8;
 
@@ -307,6 +310,10 @@ __device__ __forceinline__ float fold_partial(float M, float num, float den, flo
 //     head) row: prefix partition p in slot p, private partition p in slot
 //     ceil(prefix / prefix partition) + p. The last partition to finish for a
 //     (sequence, KV head) merges all of that row set's slots.
+//   kModeAppend: decode as kModeDecode, and sequence s's newest token (position
+//     L - 1) is appended first: its K and V rows come from k_new / v_new
+//     [B, Hkv, D], are written to the slot the block table gives, and are used
+//     from LDS (the copy in the pool is not read back).
 template <typename T, int D, int GT, bool F8, int MODE>
 __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int tid, int unit, int s, int part,
                                             int p_pre) {
@@ -317,6 +324,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   static_assert(!F8 || C::kPvMfma, "FP8 pools need a 16-bit query type");
   static_assert(!RM || (GT == 16 && C::kPvMfma), "chunk rows: 16-row tiles, 16-bit types");
   static_assert(MODE != kModeSuffix || C::kPvMfma, "shared-prefix decode: 16-bit types");
+  static_assert(MODE != kModeAppend || (C::kPvMfma && !F8), "append: 16-bit pools");
   constexpr int kKvBytes = F8 ? 1 : (int)sizeof(T);     // bytes per stored element
   constexpr int kL = kTileTokens * D * kKvBytes / (16 * 64);  // 16-byte loads per lane per K (or V) tile
   constexpr int kChKV = D * kKvBytes / 16;               // 16-byte chunks per stored token row
@@ -415,6 +423,16 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
       if (u < C::kQChunks && u / kCh < nh) qv[i] = qblk[u];
     }
   }
+  // append mode: threads 0 .. 2 kCh - 1 fetch the new K (then V) row chunks of
+  // (s, g) with q, whatever partition this is (a few hundred bytes), so their
+  // wait is the one q needs anyway
+  u32x4_t new_chunk = u32x4_t{0u, 0u, 0u, 0u};
+  if constexpr (MODE == kModeAppend) {
+    if (tid < 2 * kCh) {
+      const u32x4_t *src = static_cast<const u32x4_t *>(tid < kCh ? a.k_new : a.v_new);
+      new_chunk = src[((int64_t)s * a.n_kv_heads + g) * kCh + (tid % kCh)];
+    }
+  }
   // no query rows: empty chunk, past its last row, or a bad range
   if (RM && nh == 0) return;
   // shared mode: members of the item (whole members only: G divides 16), and
@@ -495,6 +513,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   if (start >= ctx) return;
   const int end = min(ctx, start + P);
   const int nparts = (ctx - tok0 + P - 1) / P;
+  // append mode: this item holds the newest token when its partition is the
+  // sequence's last
+  const bool holds_new = MODE == kModeAppend && end == L;
+  const int tok_new = L - 1;
   // shared mode: slot of this partition, and slot totals per member
   //   prefix partitions of a member: ceil(prefix / prefix partition)
   //   private partitions: ceil((L - prefix) / partition)
@@ -652,6 +674,16 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
       }
     }
     }
+    if constexpr (MODE == kModeAppend) {
+      // the newest token's rows replace what the tile load found in its slot
+      if (holds_new && ti == tok_new / kTileTokens) {  // uniform
+        const int tr = tok_new % kTileTokens;
+        const u32x4_t *nr = reinterpret_cast<const u32x4_t *>(smem + C::kNewOff);
+        if (lane < kCh) kst[kst_slot<kCh>(tr, lane)] = nr[lane];
+        else if (lane < 2 * kCh)
+          reinterpret_cast<u32x4_t *>(vst)[tr * kCh + ((lane - kCh) ^ vst_swz<kCh>(tr))] = nr[lane];
+      }
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -783,6 +815,17 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
     if (u < C::kQChunks)
       reinterpret_cast<u32x4_t *>(smem + C::kQOff)[kst_slot<kCh>(u / kCh, u % kCh)] = qv[i];
   }
+  // append mode: the new rows go to LDS for the tile that holds the token;
+  // the pool copy (head chunk 0 only, at the slot the table gives) is stored
+  // after the tile loop, so no wait on it sits in front of the K/V loads
+  int new_phys = -1;
+  if constexpr (MODE == kModeAppend) {
+    if (holds_new) {
+      if (tid < 2 * kCh) reinterpret_cast<u32x4_t *>(smem + C::kNewOff)[tid] = new_chunk;
+      const int phys = __builtin_amdgcn_readlane(btv, (tok_new >> a.block_shift) - jb);
+      if (hc == 0 && phys >= 0 && (int64_t)phys < a.num_blocks) new_phys = phys;
+    }
+  }
   int *mflag = reinterpret_cast<int *>(smem + C::kMemOff);  // shared mode: [16] flags
   int *mtot = mflag + 16;                                     // [16] slot totals per member
   if constexpr (SH) {
@@ -795,6 +838,14 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
     for (int ti = tb + wave; ti < te; ti += kNW) {
       load_tile(ti, rg);
       process(ti, rg, -1);
+    }
+  }
+
+  if constexpr (MODE == kModeAppend) {
+    if (new_phys >= 0 && tid < 2 * kCh) {
+      u32x4_t *dst = static_cast<u32x4_t *>(const_cast<void *>(tid < kCh ? a.k_pool : a.v_pool));
+      dst[((int64_t)new_phys * kv_stride_blk + (int64_t)g * a.block_size + (tok_new & (a.block_size - 1))) * kCh +
+          (tid % kCh)] = reinterpret_cast<const u32x4_t *>(smem + C::kNewOff)[tid];
     }
   }
 
@@ -961,13 +1012,18 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
     if (SH && !mflag[h / G]) continue;  // this member is merged by another partition
     const int tot = SH ? mtot[h / G] : nparts;
     const int own = SH ? sbase + part : part;
+    // the partials in slot order, this partition's own from registers: the
+    // sums do not depend on which partition happened to finish last
     float2 oml[kFusedMergeParts];
     float ox[kFusedMergeParts];
 #pragma unroll
     for (int p = 0; p < kFusedMergeParts; ++p) {
       oml[p] = make_float2(-INFINITY, 0.f);
       ox[p] = 0.f;
-      if (p < tot && p != own) {
+      if (p == own) {
+        oml[p] = make_float2(rM[k], rden[k]);
+        ox[p] = rnum[k];
+      } else if (p < tot) {
         const int64_t pi = prow * a.max_parts + p;
         oml[p] = __builtin_bit_cast(
             float2, __hip_atomic_load(reinterpret_cast<unsigned long long *>(a.part_ml + pi),
@@ -975,15 +1031,14 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
         ox[p] = __hip_atomic_load(a.part_acc + pi * D + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    float M = rM[k];
-    bool bad = M != M;
+    float M = -INFINITY;
+    bool bad = false;
 #pragma unroll
     for (int p = 0; p < kFusedMergeParts; ++p) {
       bad |= oml[p].x != oml[p].x;
       M = fmaxf(M, oml[p].x);
     }
-    const float f0 = rM[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(rM[k] - M);
-    float num = f0 * rnum[k], den = f0 * rden[k];
+    float num = 0.f, den = 0.f;
 #pragma unroll
     for (int p = 0; p < kFusedMergeParts; ++p) {
       const float f = oml[p].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(oml[p].x - M);
@@ -1469,6 +1524,36 @@ hipError_t launch_shared_fused(DType dt, int head_dim, bool fp8, const DecodeArg
                                 : launch_shared_fused_t<_Float16, false>(head_dim, a, stream);
     case DType::BF16: return fp8 ? launch_shared_fused_t<__bf16, true>(head_dim, a, stream)
                                  : launch_shared_fused_t<__bf16, false>(head_dim, a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_append_td(int gt, const DecodeArgs &a, hipStream_t stream) {
+  switch (gt) {
+    case 1: return launch_t<T, D, 1, false, kModeAppend>(a, stream);
+    case 2: return launch_t<T, D, 2, false, kModeAppend>(a, stream);
+    case 4: return launch_t<T, D, 4, false, kModeAppend>(a, stream);
+    case 8: return launch_t<T, D, 8, false, kModeAppend>(a, stream);
+    case 16: return launch_t<T, D, 16, false, kModeAppend>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+hipError_t launch_append_t(int head_dim, int gt, const DecodeArgs &a, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_append_td<T, 64>(gt, a, stream);
+    case 128: return launch_append_td<T, 128>(gt, a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_append(DType dt, int head_dim, const DecodeArgs &a, hipStream_t stream) {
+  const int gt = decode_head_tile(a.group);
+  switch (dt) {
+    case DType::F16: return launch_append_t<_Float16>(head_dim, gt, a, stream);
+    case DType::BF16: return launch_append_t<__bf16>(head_dim, gt, a, stream);
     default: return hipErrorInvalidValue;
   }
 }

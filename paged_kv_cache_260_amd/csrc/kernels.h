@@ -70,6 +70,10 @@ struct DecodeArgs {
   int32_t num_groups;
   int32_t prefix_partition_tokens;  // the shortest allowed (the kernel may lengthen it)
   int32_t prefix_partition_fixed;   // nonzero: use prefix_partition_tokens as given
+  // Decode with append (launch_decode_append): the newest token's K and V
+  // rows, [num_seqs, n_kv_heads, head_dim] of the pool type
+  const void *k_new;
+  const void *v_new;
 };
 
 // Largest partition count merged inside the decode kernel; longer tables use
@@ -133,6 +137,10 @@ hipError_t launch_shared_prefix(DType dt, int head_dim, bool fp8, const DecodeAr
 // heads per KV head <= 16; dt is F16 or BF16; fp8 selects e4m3 pools with
 // a.k_scale / a.v_scale (also for launch_shared_prefix).
 hipError_t launch_shared_fused(DType dt, int head_dim, bool fp8, const DecodeArgs &a, hipStream_t stream);
+
+// Decode that first appends each sequence's newest token (position
+// seq_lens[s] - 1) from a.k_new / a.v_new into its slot; dt is F16 or BF16.
+hipError_t launch_decode_append(DType dt, int head_dim, const DecodeArgs &a, hipStream_t stream);
 
 // Same over FP8 (OCP e4m3) pools with a.k_scale / a.v_scale; dt (query and
 // output) must be F16 or BF16.

@@ -52,7 +52,7 @@ def source_hash(paths=DECODE_SRCS) -> str:
 
 # the decode kernel's last template argument: what its work items' rows are
 _DECODE_MODES = {"0": "", "1": " (chunk rows)", "2": " (shared prefix)", "3": " (private tokens)",
-                 "4": " (shared prefix, one launch)"}
+                 "4": " (shared prefix, one launch)", "5": " (append)"}
 
 
 def short_name(name: str) -> str:
@@ -116,8 +116,9 @@ def summarize(name, command, stats_csv, fetch_csv, write_csv, algorithmic_bytes,
             return sum(v) / len(v) if v else 0.0
 
         per_kernel = {}
-        for k in CALL_KERNELS:
-            if not fetch.get(k):
+        # the call's kernels under their labels (the decode kernel carries its mode)
+        for k in sorted(fetch):
+            if not any(k == c or k.startswith(c + " (") for c in CALL_KERNELS):
                 continue
             per_kernel[k] = {"fetch_kib_raw": avg(fetch, k), "write_kib_raw": avg(write, k),
                              "fetch_bytes": avg(fetch, k) * f_scale * 1024,
@@ -126,7 +127,7 @@ def summarize(name, command, stats_csv, fetch_csv, write_csv, algorithmic_bytes,
         result.update({"fetch_scale": f_scale, "write_scale": w_scale, "per_kernel": per_kernel,
                        "traffic_bytes_per_call": traffic,
                        "traffic_over_algorithmic": traffic / algorithmic_bytes})
-        t = [f"# {name}: HBM traffic of one paged_attn_decode call", "",
+        t = [f"# {name}: HBM traffic of one decode call", "",
              "Two rocprofv3 counter runs (repository root), one per counter:", "",
              "```", fetch_command or "(FETCH_SIZE run)", write_command or "(WRITE_SIZE run)", "```", "",
              "Counters are KiB per dispatch. Scale: the",
@@ -140,7 +141,8 @@ def summarize(name, command, stats_csv, fetch_csv, write_csv, algorithmic_bytes,
             t.append(f"| {k} | {v['fetch_kib_raw']:.0f} | {v['write_kib_raw']:.0f} | "
                      f"{v['fetch_bytes'] / 1e6:.2f} | {v['write_bytes'] / 1e6:.2f} |")
         t += ["", f"Total per call: {traffic / 1e6:.2f} MB against {algorithmic_bytes / 1e6:.2f} MB "
-              f"algorithmic (K/V + Q + O): {traffic / algorithmic_bytes:.3f}x.",
+              f"algorithmic (K/V + Q + O, plus the stored new rows for the append call): "
+              f"{traffic / algorithmic_bytes:.3f}x.",
               f"Decode source hash: `{result['decode_source_hash']}`."]
         with open(os.path.join(out, f"{name}_traffic.md"), "w") as f:
             f.write("\n".join(t) + "\n")

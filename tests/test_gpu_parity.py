@@ -194,20 +194,26 @@ def test_random_shapes(i, H, Hkv, D, BS, dtype):
 def test_batch_sizes_and_repeated_calls(num_seqs):
     """Batch sizes around the 64-sequence chunks of the longest-first item order
     and its 256-sequence limit; 32 KV heads so a workgroup takes several items.
-    Two calls in a row must agree with the oracle (the in-kernel merge leaves its
-    arrival counters at zero)."""
+    Repeated calls must agree with the oracle (the in-kernel merge leaves its
+    arrival counters at zero) and with each other bit for bit: the merge sums
+    the partitions in a fixed order, whichever finishes last."""
     say(f"batch of {num_seqs}")
     w = workloads.random_case(4000 + num_seqs, num_seqs=num_seqs, n_heads=32, n_kv_heads=32,
                               head_dim=64, block_size=16, dtype=torch.bfloat16, max_len=2600,
                               poison=True)
     g = OnGpu(w)
     ref = oracle_decode(w, w.seq_lens, w.k_pool, w.v_pool)
-    for call in range(2):
+    first = None
+    for call in range(4):
         out = g.decode()
         torch.cuda.synchronize()
         err = max_abs_err(out, ref)
         say(f"  call {call}: max abs err {err:.3e}")
         assert err <= TOL[w.dtype]
+        if first is None:
+            first = out.clone()
+        else:
+            assert torch.equal(out.view(torch.int16), first.view(torch.int16))
 
 
 @pytest.mark.parametrize("partition", [192, 176])
