@@ -415,7 +415,11 @@ def main():
     dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
     log(f"[bench] wall {wall * 1e3 / K:.4f} ms/step, events {ms_step:.4f} ms/step")
 
-    dec_bytes = (accounting.decode_kv_bytes(lens1, w.n_kv_heads, w.head_dim, e_kv)
+    # compulsory bytes: K/V of each distinct cached token slot once (blocks that
+    # several tables share, as in the shared-prompt workload, count once), Q, O
+    uniq = accounting.unique_kv_tokens(lens1, w.block_tables, w.block_size)
+    logical_kv = accounting.decode_kv_bytes(lens1, w.n_kv_heads, w.head_dim, e_kv)
+    dec_bytes = (uniq * w.n_kv_heads * w.head_dim * 2 * e_kv
                  + accounting.decode_qo_bytes(w.num_seqs, w.n_heads, w.head_dim, e))
     n_written = int((w.slot_mapping >= 0).sum())
     # the step's compulsory bytes: decode at the new lengths (which reads each
@@ -460,6 +464,7 @@ def main():
                       "p50": round(float(np.percentile(dec_ms, 50)) * 1e3, 3),
                       "p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 3)},
         "step_bytes": int(step_bytes),
+        "logical_kv_bytes": int(logical_kv),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if fp8 else measured_traffic(args.config, fused),

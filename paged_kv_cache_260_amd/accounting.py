@@ -66,12 +66,19 @@ def write_bytes(num_written: int, n_kv_heads: int, head_dim: int, elem_bytes: in
     return 4 * num_written * n_kv_heads * head_dim * elem_bytes
 
 
-def decode_append_bytes(seq_lens_after, num_written, n_heads, n_kv_heads, head_dim, elem_bytes) -> int:
+def decode_append_bytes(seq_lens_after, num_written, n_heads, n_kv_heads, head_dim, elem_bytes,
+                        block_tables=None, block_size=None) -> int:
     """Compulsory bytes of one decode step that appends each sequence's new
     token and attends over all ``L + 1`` tokens: the decode bytes at the new
     lengths (the new K/V rows are read once, as part of them) plus the new rows
-    stored into the pools (``2 * n * Hkv * D * e``)."""
-    return (decode_compulsory_bytes(seq_lens_after, n_heads, n_kv_heads, head_dim, elem_bytes)
+    stored into the pools (``2 * n * Hkv * D * e``). With the block tables, K/V
+    bytes count each distinct cached slot once (shared prefix blocks)."""
+    if block_tables is None:
+        kv_tokens = int(np.asarray(seq_lens_after, dtype=np.int64).sum())
+    else:
+        kv_tokens = unique_kv_tokens(seq_lens_after, block_tables, block_size)
+    return (kv_tokens * n_kv_heads * head_dim * 2 * elem_bytes
+            + decode_qo_bytes(len(seq_lens_after), n_heads, head_dim, elem_bytes)
             + 2 * num_written * n_kv_heads * head_dim * elem_bytes)
 
 

@@ -80,6 +80,7 @@ template <typename T, int D, int GT> struct Cfg {
   // four waves as the MFMA A operand; rows GT..15 of the operand are zero
   static constexpr int kQOff = (kMemOff + 48 * 4 + 15) / 16 * 16;
   static constexpr int kQChunks = GT * kCh;
+  static constexpr int kQPer = (kQChunks + kNW * 64 - 1) / (kNW * 64);  // Q chunks per thread
   // append mode: the newest token's K and V rows (2 kCh chunks)
   static constexpr int kNewOff = kQOff + kQChunks * 16;
   static constexpr int kSmem = kNewOff + 2 * kCh * 16;
@@ -109,6 +110,20 @@ constexpr int kModeShared = 4;
 constexpr int kModeAppend = 5;
 constexpr int kCompactChunks = kCompactSeqs / 64;
 constexpr int kRemBuckets = 8;
+
+// The first loads of a plain decode or append item: the sequence length, the
+// partition's block-table entries (one per lane), this thread's query chunks
+// and (append) the new K/V row chunks. None of the addresses depends on the
+// length. The item loop issues them for the next item as soon as the current
+// item's tile loop is done, so they are in flight while the workgroup merges
+// and writes the current item instead of after it.
+template <int QPER> struct ItemHead {
+  int L;
+  int btv_raw;
+  u32x4_t qv[QPER];
+  u32x4_t new_chunk;
+  bool ready;  // uniform: the fields hold the loads of the item about to run
+};
 
 struct ItemPlan {
   int fb[kCompactChunks];  // per lane: (full partitions << 4) | bucket, bucket 15 = no sequence
@@ -314,13 +329,52 @@ __device__ __forceinline__ float fold_partial(float M, float num, float den, flo
 //     L - 1) is appended first: its K and V rows come from k_new / v_new
 //     [B, Hkv, D], are written to the slot the block table gives, and are used
 //     from LDS (the copy in the pool is not read back).
+// Issues the first loads of decode / append item (s, part) of `unit`
+// (partitions of partition_tokens from token 0; Q rows past the head group
+// are zero).
+template <typename T, int D, int GT, int MODE>
+__device__ __forceinline__ void load_item_head(const DecodeArgs &a, int tid, int unit, int s, int part,
+                                               ItemHead<Cfg<T, D, GT>::kQPer> &h) {
+  using C = Cfg<T, D, GT>;
+  constexpr int kCh = C::kCh;
+  const int lane = tid & 63;
+  const int g = unit / a.head_chunks;
+  const int hc = unit - g * a.head_chunks;
+  const int nh = min(GT, a.group - hc * GT);
+  const int jb = (part * a.partition_tokens) >> a.block_shift;
+  const int32_t *bt_row = a.block_tables + (int64_t)s * a.max_blocks;
+  h.btv_raw = jb + lane < a.max_blocks ? bt_row[jb + lane] : 0;
+  const u32x4_t *qblk = reinterpret_cast<const u32x4_t *>(static_cast<const T *>(a.q) +
+                                                          ((int64_t)s * a.n_heads + g * a.group + hc * GT) * D);
+#pragma unroll
+  for (int i = 0; i < C::kQPer; ++i) {
+    const int u = tid + i * C::kNW * 64;
+    h.qv[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if (u < C::kQChunks && u / kCh < nh) h.qv[i] = qblk[u];
+  }
+  // append mode: threads 0 .. 2 kCh - 1 fetch the new K (then V) row chunks
+  // of (s, g), whatever partition this is (a few hundred bytes)
+  h.new_chunk = u32x4_t{0u, 0u, 0u, 0u};
+  if constexpr (MODE == kModeAppend) {
+    if (tid < 2 * kCh) {
+      const u32x4_t *src = static_cast<const u32x4_t *>(tid < kCh ? a.k_new : a.v_new);
+      h.new_chunk = src[((int64_t)s * a.n_kv_heads + g) * kCh + (tid % kCh)];
+    }
+  }
+  h.L = a.seq_lens[s];
+  h.ready = true;
+}
+
 template <typename T, int D, int GT, bool F8, int MODE>
 __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int tid, int unit, int s, int part,
-                                            int p_pre) {
+                                            int p_pre, ItemHead<Cfg<T, D, GT>::kQPer> &hd, int s_next,
+                                            int part_next) {
   using C = Cfg<T, D, GT>;
   // rows mode: item rows are (token or member, head) pairs
   constexpr bool RM = MODE == kModeChunk || MODE == kModePrefix || MODE == kModeShared;
   constexpr bool SH = MODE == kModeShared;
+  // plain decode and append: the first loads come from (or go into) `hd`
+  constexpr bool kHead = MODE == kModeDecode || MODE == kModeAppend;
   static_assert(!F8 || C::kPvMfma, "FP8 pools need a 16-bit query type");
   static_assert(!RM || (GT == 16 && C::kPvMfma), "chunk rows: 16-row tiles, 16-bit types");
   static_assert(MODE != kModeSuffix || C::kPvMfma, "shared-prefix decode: 16-bit types");
@@ -397,14 +451,26 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   // these addresses depends on the length. Table entries past the sequence
   // (but inside the row) are read and ignored. Prefix mode reads the table
   // of the group's first member.
-  const int32_t *bt_row =
-      a.block_tables + (int64_t)(MODE == kModePrefix || SH ? (bad_rows ? 0 : q0) : s) * a.max_blocks;
   const int jb = start >> a.block_shift;
-  const int btv_raw = jb + lane < a.max_blocks ? bt_row[jb + lane] : 0;
   // Q chunks of this thread: chunk u = tid + 256 i of the GT x kCh head-row
   // block (rows past nh are zero)
-  constexpr int kQPer = (C::kQChunks + kNW * 64 - 1) / (kNW * 64);
+  constexpr int kQPer = C::kQPer;
   u32x4_t qv[kQPer];
+  int btv_raw;
+  u32x4_t new_chunk = u32x4_t{0u, 0u, 0u, 0u};
+  int L_head = 0;
+  if constexpr (kHead) {
+    if (!hd.ready) load_item_head<T, D, GT, MODE>(a, tid, unit, s, part, hd);
+    btv_raw = hd.btv_raw;
+#pragma unroll
+    for (int i = 0; i < kQPer; ++i) qv[i] = hd.qv[i];
+    new_chunk = hd.new_chunk;
+    L_head = hd.L;
+    hd.ready = false;
+  } else {
+  const int32_t *bt_row =
+      a.block_tables + (int64_t)(MODE == kModePrefix || SH ? (bad_rows ? 0 : q0) : s) * a.max_blocks;
+  btv_raw = jb + lane < a.max_blocks ? bt_row[jb + lane] : 0;
   if constexpr (RM) {
 #pragma unroll
     for (int i = 0; i < kQPer; ++i) {
@@ -423,15 +489,6 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
       if (u < C::kQChunks && u / kCh < nh) qv[i] = qblk[u];
     }
   }
-  // append mode: threads 0 .. 2 kCh - 1 fetch the new K (then V) row chunks of
-  // (s, g) with q, whatever partition this is (a few hundred bytes), so their
-  // wait is the one q needs anyway
-  u32x4_t new_chunk = u32x4_t{0u, 0u, 0u, 0u};
-  if constexpr (MODE == kModeAppend) {
-    if (tid < 2 * kCh) {
-      const u32x4_t *src = static_cast<const u32x4_t *>(tid < kCh ? a.k_new : a.v_new);
-      new_chunk = src[((int64_t)s * a.n_kv_heads + g) * kCh + (tid % kCh)];
-    }
   }
   // no query rows: empty chunk, past its last row, or a bad range
   if (RM && nh == 0) return;
@@ -447,7 +504,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   }
   // Prefix mode: a prefix that is empty or not a whole number of blocks is
   // left to the suffix launch (nothing to fold, or NaN rows).
-  const int L = MODE == kModePrefix || pre_item ? a.prefix_lens[q0] : (SH ? a.seq_lens[q0] : a.seq_lens[s]);
+  const int L = kHead ? L_head
+                      : (MODE == kModePrefix || pre_item ? a.prefix_lens[q0] : (SH ? a.seq_lens[q0] : a.seq_lens[s]));
   const int64_t cap = (int64_t)a.max_blocks * a.block_size;
   bool bad_len = L < 0 || (int64_t)L > cap;
   if constexpr (MODE == kModeChunk) bad_len |= L < nq || q0 < 0;
@@ -841,6 +899,14 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
     }
   }
 
+  // the next item's first loads fly while this one is merged and written
+  if constexpr (kHead) {
+    if (s_next >= 0) {
+      load_item_head<T, D, GT, MODE>(a, tid, unit, s_next, part_next, hd);
+    } else {
+      hd = ItemHead<kQPer>{};
+    }
+  }
   if constexpr (MODE == kModeAppend) {
     if (new_phys >= 0 && tid < 2 * kCh) {
       u32x4_t *dst = static_cast<u32x4_t *>(const_cast<void *>(tid < kCh ? a.k_pool : a.v_pool));
@@ -1087,20 +1153,34 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT>()))) void paged
   ItemPlan plan;
   plan.p_pre = a.prefix_partition_tokens;
   if (compact) make_plan<MODE>(a, plan);
-  for (int round = 0;; ++round) {
-    int s, part;
+  ItemHead<Cfg<T, D, GT>::kQPer> hd{};
+  hd.ready = false;
+  // item j of this workgroup's walk (compact plans), or -1 past its end
+  auto item_of = [&](int round) -> int64_t {
+    const int G = a.wgs_per_unit;
+    const int64_t j = (int64_t)round * G + ((round & 1) ? G - 1 - w : w);
+    return j < plan.items ? j : -1;
+  };
+  // this round's item (s < 0: none), and the next one, whose first loads the
+  // current item issues
+  int s = -1, part = 0;
+  if (compact) {
+    const int64_t j = item_of(0);
+    if (j >= 0) locate_item(plan, a.num_seqs, (int)j, s, part);
+  } else {
+    part = w / a.num_seqs;
+    s = (w % a.num_seqs + a.num_seqs - part % a.num_seqs) % a.num_seqs;
+  }
+  for (int round = 0; s >= 0; ++round) {
+    int s_next = -1, part_next = 0;
     if (compact) {
-      const int G = a.wgs_per_unit;
-      const int64_t j = (int64_t)round * G + ((round & 1) ? G - 1 - w : w);
-      if (j >= plan.items) break;
-      locate_item(plan, a.num_seqs, (int)j, s, part);
-    } else {
-      if (round > 0) break;
-      part = w / a.num_seqs;
-      s = (w % a.num_seqs + a.num_seqs - part % a.num_seqs) % a.num_seqs;
+      const int64_t jn = item_of(round + 1);
+      if (jn >= 0) locate_item(plan, a.num_seqs, (int)jn, s_next, part_next);
     }
     s = __builtin_amdgcn_readfirstlane(s);
     part = __builtin_amdgcn_readfirstlane(part);
+    s_next = __builtin_amdgcn_readfirstlane(s_next);
+    part_next = __builtin_amdgcn_readfirstlane(part_next);
     if (round > 0) __syncthreads();  // the previous item's merge has read every wave's LDS
     // An opaque copy of the thread index: lane-derived addresses are then
     // recomputed per item instead of being hoisted out of the item loop and
@@ -1108,7 +1188,10 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT>()))) void paged
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     // prefix partition length (shared mode): the plan's, or the host's minimum
-    decode_item<T, D, GT, F8, MODE>(a, smem, tid, unit, s, part, compact ? plan.p_pre : a.prefix_partition_tokens);
+    decode_item<T, D, GT, F8, MODE>(a, smem, tid, unit, s, part, compact ? plan.p_pre : a.prefix_partition_tokens,
+                                    hd, s_next, part_next);
+    s = s_next;
+    part = part_next;
   }
 }
 

@@ -149,3 +149,10 @@ def test_decode_bytes_closed_form():
     assert accounting.decode_table_bytes(lens, 16) == 4 * (1 + 7 + 1) + 12
     bt = np.array([[5, 6, -1], [5, 7, -1]])
     assert accounting.unique_kv_tokens([20, 20], bt, 16) == 16 + 4 + 4
+    # append step: K/V at the new lengths (shared first block once), Q and O,
+    # plus the two new rows stored per sequence and KV head
+    per_tok = 8 * 128 * 2 * 2
+    assert accounting.decode_append_bytes([20, 20], 2, 32, 8, 128, 2) == (
+        40 * per_tok + 2 * 2 * 32 * 128 * 2 + 2 * 2 * 8 * 128 * 2)
+    assert accounting.decode_append_bytes([20, 20], 2, 32, 8, 128, 2, bt, 16) == (
+        24 * per_tok + 2 * 2 * 32 * 128 * 2 + 2 * 2 * 8 * 128 * 2)
