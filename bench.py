@@ -289,8 +289,9 @@ def bench_shared_prefix(args, dev):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps first (a few hundred let the GPU clocks settle)")
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5],
                     help="workload (3 = GQA bf16 batch 128, the headline)")
     ap.add_argument("--replicas", type=int, default=0, help="pool copies to rotate (0 = auto)")

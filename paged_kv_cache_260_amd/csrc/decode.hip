@@ -48,6 +48,29 @@ namespace {
 
 using namespace attn;
 
+// Batches of up to kCompactSeqs sequences (entities) take the longest-first
+// item order below, built per workgroup in LDS.
+constexpr int kCompactSeqs = 256;
+constexpr int kCompactChunks = kCompactSeqs / 64;
+constexpr int kRemBuckets = 8;
+
+// The plan in LDS (int offsets from Cfg::kPlanOff), kCompactSeqs entries each:
+//   incl: inclusive prefix of the full-partition counts in sequence order
+//         (entries past the batch hold the total), so entity e owns full items
+//         [incl[e - 1], incl[e]);
+//   rank: position of the entity's last partition in the remainder list
+//         (past the batch: INT_MAX);
+//   cnt:  per (bucket b, chunk c) entity counts at b * 4 + c, then the chunks'
+//         full-partition totals at 36 + c;
+//   aux:  shared mode, the chunks' longest private parts.
+constexpr int kPlanIncl = 0;
+constexpr int kPlanRank = kCompactSeqs;
+constexpr int kPlanCnt = 2 * kCompactSeqs;
+constexpr int kPlanAux = kPlanCnt + (kRemBuckets + 1) * kCompactChunks + kCompactChunks;
+constexpr int kPlanInts = kPlanAux + kCompactChunks;
+static_assert(kDecodeWaves == kCompactChunks, "one wave per 64-entity chunk of the plan");
+static_assert((kRemBuckets + 1) * kCompactChunks <= 64, "bucket counts fit one wave");
+
 template <typename T, int D, int GT> struct Cfg {
   static constexpr int kEpc = Elem<T>::kPerChunk;        // elements per 16-byte chunk
   static constexpr int kCh = D / kEpc;                   // chunks per token row
@@ -83,7 +106,9 @@ template <typename T, int D, int GT> struct Cfg {
   static constexpr int kQPer = (kQChunks + kNW * 64 - 1) / (kNW * 64);  // Q chunks per thread
   // append mode: the newest token's K and V rows (2 kCh chunks)
   static constexpr int kNewOff = kQOff + kQChunks * 16;
-  static constexpr int kSmem = kNewOff + 2 * kCh * 16;
+  // the item order of compact plans (make_plan), kPlanInts ints
+  static constexpr int kPlanOff = (kNewOff + 2 * kCh * 16 + 15) / 16 * 16;
+  static constexpr int kSmem = kPlanOff + kPlanInts * 4;
   static_assert(kCh % 4 == 0 && 64 % kCh == 0, "head_dim must give 8, 16 or 32 chunks");
   static_assert(!kPvMfma || kCh == 8 || kCh == 16, "MFMA P*V path: 8 or 16 chunks per row");
   static_assert(GT >= 1 && GT <= 16, "head tile");
@@ -96,10 +121,9 @@ template <typename T, int D, int GT> struct Cfg {
 //   2. the last partitions, in kRemBuckets buckets of decreasing length
 //      (sequence order within a bucket); zero-length and invalid sequences
 //      come last (their one item writes the zero or NaN row).
-// Each wave derives the order from the lengths by itself (wave-wide scans and
-// ballots over 64-sequence chunks held in registers), so no workgroup-wide
-// synchronisation is needed.
-constexpr int kCompactSeqs = 256;
+// Every workgroup derives the order from the lengths by itself (make_plan:
+// one wave per 64-sequence chunk, wave-wide scans and ballots, two barriers)
+// into LDS, where locate_item finds an item with four reads and ballots.
 
 // What a work item's rows are (decode_item).
 constexpr int kModeDecode = 0;
@@ -108,8 +132,6 @@ constexpr int kModePrefix = 2;
 constexpr int kModeSuffix = 3;
 constexpr int kModeShared = 4;
 constexpr int kModeAppend = 5;
-constexpr int kCompactChunks = kCompactSeqs / 64;
-constexpr int kRemBuckets = 8;
 
 // The first loads of a plain decode or append item: the sequence length, the
 // partition's block-table entries (one per lane), this thread's query chunks
@@ -126,11 +148,11 @@ template <int QPER> struct ItemHead {
 };
 
 struct ItemPlan {
-  int fb[kCompactChunks];  // per lane: (full partitions << 4) | bucket, bucket 15 = no sequence
-  int full_items;          // full partitions of the batch (uniform)
-  int items;               // all items of one unit (uniform)
-  int p_pre;               // shared mode: partition length of the prefix entities (uniform)
+  int full_items;  // full partitions of the batch (uniform)
+  int items;       // all items of one unit (uniform)
+  int p_pre;       // shared mode: partition length of the prefix entities (uniform)
 };
+
 
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 #pragma unroll
@@ -157,130 +179,116 @@ __device__ __forceinline__ int shared_prefix_partition(const DecodeArgs &a, int 
   return min(p, kMaxPartitionBlocks * bs);
 }
 
-template <int MODE> __device__ __forceinline__ void make_plan(const DecodeArgs &a, ItemPlan &pl) {
+// Builds the plan in LDS with the whole workgroup: wave c takes entities
+// [64 c, 64 c + 64) (one load round trip), counts them per bucket, and after
+// one barrier every wave turns the chunk counts into positions; a second
+// barrier publishes them. Every workgroup computes the same plan.
+template <int MODE> __device__ __forceinline__ void make_plan(const DecodeArgs &a, ItemPlan &pl, int *sp) {
   const int lane = threadIdx.x & 63;
+  const int c = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // this wave's chunk
+  const int e = c * 64 + lane;                                            // this lane's entity
   const int B = a.num_seqs;
+  const bool in = e < B;
+  const int ec = min(e, B - 1);
   const int P = a.partition_tokens;
   const int64_t max_tok = (int64_t)a.max_blocks * a.block_size;
-  // all chunk loads first (clamped index, no branches), so they are in flight
-  // together and one wait covers them
-  int Ls[kCompactChunks];
-  int Pe[kCompactChunks];  // partition length of each lane's entity
-#pragma unroll
-  for (int c = 0; c < kCompactChunks; ++c) Pe[c] = P;
+  int L;       // tokens the entity's items walk
+  int Pe = P;  // its partition length
+  pl.p_pre = a.prefix_partition_tokens;
   if constexpr (MODE == kModeShared) {
     // entities: the groups' prefixes, then the sequences' private tokens
     const int ng = a.num_groups;
-    int first[kCompactChunks], len[kCompactChunks], pre[kCompactChunks];
-#pragma unroll
-    for (int c = 0; c < kCompactChunks; ++c) {
-      const int e = min(c * 64 + lane, B - 1);
-      first[c] = e < ng ? a.query_start_loc[e] : e - ng;
-    }
-#pragma unroll
-    for (int c = 0; c < kCompactChunks; ++c) {
-      const int m = min(max(first[c], 0), a.member_seqs - 1);
-      len[c] = a.seq_lens[m];
-      pre[c] = a.prefix_lens[m];
-    }
-    int max_private = 0;
-#pragma unroll
-    for (int c = 0; c < kCompactChunks; ++c) {
-      const bool is_pre = c * 64 + lane < ng;
-      Ls[c] = is_pre ? pre[c] : (pre[c] >= 0 && pre[c] <= len[c] ? len[c] - pre[c] : -1);
-      if (!is_pre && c * 64 + lane < B && (int64_t)len[c] <= max_tok) max_private = max(max_private, Ls[c]);
-    }
+    const bool is_pre = e < ng;
+    const int first = ec < ng ? a.query_start_loc[ec] : ec - ng;
+    const int m = min(max(first, 0), a.member_seqs - 1);
+    const int len = a.seq_lens[m];
+    const int pre = a.prefix_lens[m];
+    L = is_pre ? pre : (pre >= 0 && pre <= len ? len - pre : -1);
+    int max_private = !is_pre && in && (int64_t)len <= max_tok ? max(L, 0) : 0;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) max_private = max(max_private, __shfl_xor(max_private, d, 64));
+    if (lane == 0) sp[kPlanAux + c] = max_private;
+    __syncthreads();
+#pragma unroll
+    for (int cc = 0; cc < kCompactChunks; ++cc) max_private = max(max_private, sp[kPlanAux + cc]);
     pl.p_pre = __builtin_amdgcn_readfirstlane(shared_prefix_partition(a, max_private));
-#pragma unroll
-    for (int c = 0; c < kCompactChunks; ++c) Pe[c] = c * 64 + lane < ng ? pl.p_pre : P;
+    Pe = is_pre ? pl.p_pre : P;
   } else if constexpr (MODE == kModePrefix) {
-    int first[kCompactChunks];
-#pragma unroll
-    for (int c = 0; c < kCompactChunks; ++c) first[c] = a.query_start_loc[min(c * 64 + lane, B - 1)];
-#pragma unroll
-    for (int c = 0; c < kCompactChunks; ++c)
-      Ls[c] = a.prefix_lens[min(max(first[c], 0), a.member_seqs - 1)];
+    const int first = a.query_start_loc[ec];
+    L = a.prefix_lens[min(max(first, 0), a.member_seqs - 1)];
   } else if constexpr (MODE == kModeSuffix) {
-    int pre[kCompactChunks];
-#pragma unroll
-    for (int c = 0; c < kCompactChunks; ++c) {
-      Ls[c] = a.seq_lens[min(c * 64 + lane, B - 1)];
-      pre[c] = a.prefix_lens[min(c * 64 + lane, B - 1)];
-    }
-#pragma unroll
-    for (int c = 0; c < kCompactChunks; ++c) Ls[c] = pre[c] >= 0 && pre[c] <= Ls[c] ? Ls[c] - pre[c] : -1;
+    const int len = a.seq_lens[ec];
+    const int pre = a.prefix_lens[ec];
+    L = pre >= 0 && pre <= len ? len - pre : -1;
   } else {
-#pragma unroll
-    for (int c = 0; c < kCompactChunks; ++c) Ls[c] = a.seq_lens[min(c * 64 + lane, B - 1)];
+    L = a.seq_lens[ec];
   }
-  int full_sum = 0;
+  const bool ok = in && L > 0 && (int64_t)L <= max_tok;
+  const int full = ok ? (L - 1) / Pe : 0;
+  const int rem = L - full * Pe;  // 1 .. Pe when ok
+  // buckets of decreasing last-partition length; invalid and empty entities
+  // in the last one, lanes past the batch in none (partitions are at most
+  // 2^20 tokens, so the product fits 32 bits)
+  const int bucket = !in ? 15 : (ok ? (Pe - rem) * kRemBuckets / Pe : kRemBuckets);
+  const int x = wave_incl_scan(full, lane);  // inclusive, within the chunk
+  int pos_in = 0;                            // among the chunk's lanes of the same bucket
+  int my_cnt = 0;                            // lane b: the chunk's lanes in bucket b
 #pragma unroll
-  for (int c = 0; c < kCompactChunks; ++c) {
-    pl.fb[c] = 15;
-    if (c * 64 + lane < B) {
-      const int L = Ls[c];
-      const int Pc = Pe[c];
-      const bool ok = L > 0 && (int64_t)L <= max_tok;
-      const int full = ok ? (L - 1) / Pc : 0;
-      const int rem = L - full * Pc;  // 1 .. Pc when ok
-      pl.fb[c] = (full << 4) | (ok ? (int)(((int64_t)(Pc - rem) * kRemBuckets) / Pc) : kRemBuckets);
-      full_sum += full;
-    }
+  for (int b = 0; b <= kRemBuckets; ++b) {
+    const unsigned long long m = __builtin_amdgcn_ballot_w64(bucket == b);
+    if (lane == b) my_cnt = __popcll(m);
+    if (bucket == b)
+      pos_in = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
   }
-  pl.full_items = __builtin_amdgcn_readlane(wave_incl_scan(full_sum, lane), 63);
+  if (lane <= kRemBuckets) sp[kPlanCnt + lane * kCompactChunks + c] = my_cnt;
+  if (lane == 63) sp[kPlanCnt + (kRemBuckets + 1) * kCompactChunks + c] = x;
+  __syncthreads();
+  // exclusive prefix over (bucket, chunk), bucket-major: the remainder list
+  // takes bucket 0 of every chunk in chunk order, then bucket 1, ...
+  const int v = lane < (kRemBuckets + 1) * kCompactChunks ? sp[kPlanCnt + lane] : 0;
+  const int ex = wave_incl_scan(v, lane) - v;
+  int fbase = 0, ftot = 0;
+#pragma unroll
+  for (int cc = 0; cc < kCompactChunks; ++cc) {
+    const int t = sp[kPlanCnt + (kRemBuckets + 1) * kCompactChunks + cc];
+    fbase += cc < c ? t : 0;
+    ftot += t;
+  }
+  const int rbase = __shfl(ex, min(bucket, kRemBuckets) * kCompactChunks + c, 64);
+  sp[kPlanIncl + e] = in ? fbase + x : ftot;
+  sp[kPlanRank + e] = in ? rbase + pos_in : 0x7fffffff;
+  __syncthreads();
+  pl.full_items = __builtin_amdgcn_readfirstlane(ftot);
   pl.items = pl.full_items + B;
 }
 
-// Item j (< pl.items) of the order above -> (sequence, partition), uniform.
-// Written without early exits: every chunk and bucket is visited, the match
-// recorded once (an early return here made the compiler keep far more
-// registers live through the decode loop).
-__device__ __forceinline__ void locate_item(const ItemPlan &pl, int B, int j, int &s_out, int &p_out) {
+// Item j (< pl.items) of the order above -> (entity, partition), uniform:
+// the first entity whose inclusive full count passes j (full list), or the
+// entity of remainder rank j - full_items; four LDS reads and ballots.
+__device__ __forceinline__ void locate_item(const ItemPlan &pl, const int *sp, int B, int j, int &s_out,
+                                            int &p_out) {
   const int lane = threadIdx.x & 63;
-  int s_res = 0, p_res = 0;
+  const bool full_list = j < pl.full_items;  // uniform
+  const int jj = j - pl.full_items;
+  int key[kCompactChunks];
+#pragma unroll
+  for (int c = 0; c < kCompactChunks; ++c) key[c] = sp[(full_list ? kPlanIncl : kPlanRank) + c * 64 + lane];
+  int s_res = 0;
   bool found = false;
-  if (j < pl.full_items) {
-    int base = 0;
 #pragma unroll
-    for (int c = 0; c < kCompactChunks; ++c) {
-      if (c * 64 < B) {
-        const int x = wave_incl_scan(pl.fb[c] >> 4, lane);
-        const int tot = __builtin_amdgcn_readlane(x, 63);
-        if (!found && j < base + tot) {
-          const int sl = __builtin_ctzll(__builtin_amdgcn_ballot_w64(base + x > j));
-          s_res = c * 64 + sl;
-          p_res = j - (base + __builtin_amdgcn_readlane(x, sl) - (__builtin_amdgcn_readlane(pl.fb[c], sl) >> 4));
-          found = true;
-        }
-        base += tot;
-      }
-    }
-  } else {
-    int jj = j - pl.full_items;
-    for (int b = 0; b <= kRemBuckets; ++b) {
-#pragma unroll
-      for (int c = 0; c < kCompactChunks; ++c) {
-        if (c * 64 < B) {
-          const bool in = (pl.fb[c] & 15) == b;
-          const unsigned long long m = __builtin_amdgcn_ballot_w64(in);
-          const int pc = __popcll(m);
-          if (!found && jj < pc) {
-            const int below =
-                __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
-            const int sl = __builtin_ctzll(__builtin_amdgcn_ballot_w64(in && below == jj));
-            s_res = c * 64 + sl;
-            p_res = __builtin_amdgcn_readlane(pl.fb[c], sl) >> 4;
-            found = true;
-          }
-          jj -= pc;
-        }
-      }
+  for (int c = 0; c < kCompactChunks; ++c) {
+    const bool hit = c * 64 + lane < B && (full_list ? key[c] > j : key[c] == jj);
+    const unsigned long long m = __builtin_amdgcn_ballot_w64(hit);
+    if (!found && m != 0ull) {
+      s_res = c * 64 + __builtin_ctzll(m);
+      found = true;
     }
   }
-  s_out = s_res;
-  p_out = p_res;
+  const int incl = sp[kPlanIncl + s_res];
+  const int excl = s_res > 0 ? sp[kPlanIncl + s_res - 1] : 0;
+  const int p = full_list ? j - excl : incl - excl;
+  s_out = __builtin_amdgcn_readfirstlane(s_res);
+  p_out = __builtin_amdgcn_readfirstlane(max(p, 0));
 }
 
 // Output value of a row from its own un-normalised state (M, num, den) and a
@@ -1152,7 +1160,9 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT>()))) void paged
   const bool compact = a.num_seqs <= kCompactSeqs;
   ItemPlan plan;
   plan.p_pre = a.prefix_partition_tokens;
-  if (compact) make_plan<MODE>(a, plan);
+  plan.full_items = plan.items = 0;
+  int *plan_lds = reinterpret_cast<int *>(smem + Cfg<T, D, GT>::kPlanOff);
+  if (compact) make_plan<MODE>(a, plan, plan_lds);
   ItemHead<Cfg<T, D, GT>::kQPer> hd{};
   hd.ready = false;
   // item j of this workgroup's walk (compact plans), or -1 past its end
@@ -1166,7 +1176,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT>()))) void paged
   int s = -1, part = 0;
   if (compact) {
     const int64_t j = item_of(0);
-    if (j >= 0) locate_item(plan, a.num_seqs, (int)j, s, part);
+    if (j >= 0) locate_item(plan, plan_lds, a.num_seqs, (int)j, s, part);
   } else {
     part = w / a.num_seqs;
     s = (w % a.num_seqs + a.num_seqs - part % a.num_seqs) % a.num_seqs;
@@ -1175,7 +1185,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT>()))) void paged
     int s_next = -1, part_next = 0;
     if (compact) {
       const int64_t jn = item_of(round + 1);
-      if (jn >= 0) locate_item(plan, a.num_seqs, (int)jn, s_next, part_next);
+      if (jn >= 0) locate_item(plan, plan_lds, a.num_seqs, (int)jn, s_next, part_next);
     }
     s = __builtin_amdgcn_readfirstlane(s);
     part = __builtin_amdgcn_readfirstlane(part);
