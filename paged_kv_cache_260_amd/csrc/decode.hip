@@ -154,12 +154,17 @@ struct ItemPlan {
 };
 
 
-__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
+// Inclusive prefix sum over the wave with DPP (no LDS round trips): shifts
+// right by 1, 2, 4 and 8 within each 16-lane row (lanes shifted in from
+// outside the row read 0), then row 0's total added to row 1 and row 2's to
+// row 3 (row_bcast:15), then rows 0-1's total to rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
   return x;
 }
 
@@ -230,7 +235,7 @@ template <int MODE> __device__ __forceinline__ void make_plan(const DecodeArgs &
   // in the last one, lanes past the batch in none (partitions are at most
   // 2^20 tokens, so the product fits 32 bits)
   const int bucket = !in ? 15 : (ok ? (Pe - rem) * kRemBuckets / Pe : kRemBuckets);
-  const int x = wave_incl_scan(full, lane);  // inclusive, within the chunk
+  const int x = wave_incl_scan(full);  // inclusive, within the chunk
   int pos_in = 0;                            // among the chunk's lanes of the same bucket
   int my_cnt = 0;                            // lane b: the chunk's lanes in bucket b
 #pragma unroll
@@ -246,7 +251,7 @@ template <int MODE> __device__ __forceinline__ void make_plan(const DecodeArgs &
   // exclusive prefix over (bucket, chunk), bucket-major: the remainder list
   // takes bucket 0 of every chunk in chunk order, then bucket 1, ...
   const int v = lane < (kRemBuckets + 1) * kCompactChunks ? sp[kPlanCnt + lane] : 0;
-  const int ex = wave_incl_scan(v, lane) - v;
+  const int ex = wave_incl_scan(v) - v;
   int fbase = 0, ftot = 0;
 #pragma unroll
   for (int cc = 0; cc < kCompactChunks; ++cc) {
