@@ -54,22 +54,30 @@ constexpr int kCompactSeqs = 256;
 constexpr int kCompactChunks = kCompactSeqs / 64;
 constexpr int kRemBuckets = 8;
 
-// The plan in LDS (int offsets from Cfg::kPlanOff), kCompactSeqs entries each:
-//   incl: inclusive prefix of the full-partition counts in sequence order
-//         (entries past the batch hold the total), so entity e owns full items
-//         [incl[e - 1], incl[e]);
-//   rank: position of the entity's last partition in the remainder list
-//         (past the batch: INT_MAX);
+// The plan in LDS (int offsets from Cfg::kPlanOff):
+//   entry[e] (kCompactSeqs of them) = (incl << 8) | rank, where incl is the
+//         inclusive prefix of the full-partition counts in sequence order
+//         (entity e owns full items [incl[e - 1], incl[e]); entries past the
+//         batch hold the total) and rank the position of the entity's last
+//         partition in the remainder list (< B <= 256; never matched past the
+//         batch). compact_plan keeps incl below 2^23.
 //   cnt:  per (bucket b, chunk c) entity counts at b * 4 + c, then the chunks'
 //         full-partition totals at 36 + c;
 //   aux:  shared mode, the chunks' longest private parts.
-constexpr int kPlanIncl = 0;
-constexpr int kPlanRank = kCompactSeqs;
-constexpr int kPlanCnt = 2 * kCompactSeqs;
+constexpr int kPlanEntry = 0;
+constexpr int kPlanCnt = kCompactSeqs;
 constexpr int kPlanAux = kPlanCnt + (kRemBuckets + 1) * kCompactChunks + kCompactChunks;
 constexpr int kPlanInts = kPlanAux + kCompactChunks;
 static_assert(kDecodeWaves == kCompactChunks, "one wave per 64-entity chunk of the plan");
 static_assert((kRemBuckets + 1) * kCompactChunks <= 64, "bucket counts fit one wave");
+static_assert(kCompactSeqs <= 256, "remainder ranks take 8 bits of a plan entry");
+
+// Batches that take the longest-first plan: at most kCompactSeqs entities,
+// and few enough partitions in all that the packed prefixes fit (partitions
+// are at least 16 tokens, so the batch has fewer than 2^23 of them).
+__host__ __device__ __forceinline__ bool compact_plan(const DecodeArgs &a) {
+  return a.num_seqs <= kCompactSeqs && (int64_t)a.num_seqs * a.max_blocks * a.block_size < (int64_t(1) << 27);
+}
 
 template <typename T, int D, int GT> struct Cfg {
   static constexpr int kEpc = Elem<T>::kPerChunk;        // elements per 16-byte chunk
@@ -260,8 +268,7 @@ template <int MODE> __device__ __forceinline__ void make_plan(const DecodeArgs &
     ftot += t;
   }
   const int rbase = __shfl(ex, min(bucket, kRemBuckets) * kCompactChunks + c, 64);
-  sp[kPlanIncl + e] = in ? fbase + x : ftot;
-  sp[kPlanRank + e] = in ? rbase + pos_in : 0x7fffffff;
+  sp[kPlanEntry + e] = ((in ? fbase + x : ftot) << 8) | (in ? rbase + pos_in : 0);
   __syncthreads();
   pl.full_items = __builtin_amdgcn_readfirstlane(ftot);
   pl.items = pl.full_items + B;
@@ -277,20 +284,20 @@ __device__ __forceinline__ void locate_item(const ItemPlan &pl, const int *sp, i
   const int jj = j - pl.full_items;
   int key[kCompactChunks];
 #pragma unroll
-  for (int c = 0; c < kCompactChunks; ++c) key[c] = sp[(full_list ? kPlanIncl : kPlanRank) + c * 64 + lane];
+  for (int c = 0; c < kCompactChunks; ++c) key[c] = sp[kPlanEntry + c * 64 + lane];
   int s_res = 0;
   bool found = false;
 #pragma unroll
   for (int c = 0; c < kCompactChunks; ++c) {
-    const bool hit = c * 64 + lane < B && (full_list ? key[c] > j : key[c] == jj);
+    const bool hit = c * 64 + lane < B && (full_list ? (key[c] >> 8) > j : (key[c] & 255) == jj);
     const unsigned long long m = __builtin_amdgcn_ballot_w64(hit);
     if (!found && m != 0ull) {
       s_res = c * 64 + __builtin_ctzll(m);
       found = true;
     }
   }
-  const int incl = sp[kPlanIncl + s_res];
-  const int excl = s_res > 0 ? sp[kPlanIncl + s_res - 1] : 0;
+  const int incl = sp[kPlanEntry + s_res] >> 8;
+  const int excl = s_res > 0 ? sp[kPlanEntry + s_res - 1] >> 8 : 0;
   const int p = full_list ? j - excl : incl - excl;
   s_out = __builtin_amdgcn_readfirstlane(s_res);
   p_out = __builtin_amdgcn_readfirstlane(max(p, 0));
@@ -1162,7 +1169,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT>()))) void paged
   const int64_t lin = blockIdx.x;
   const int unit = (int)(lin % units);
   const int w = (int)(lin / units);
-  const bool compact = a.num_seqs <= kCompactSeqs;
+  const bool compact = compact_plan(a);
   ItemPlan plan;
   plan.p_pre = a.prefix_partition_tokens;
   plan.full_items = plan.items = 0;
@@ -1465,7 +1472,7 @@ hipError_t launch_t(const DecodeArgs &args, hipStream_t stream) {
   DecodeArgs a = args;
   const int64_t units = (int64_t)a.n_kv_heads * a.head_chunks;
   const int64_t max_items = (int64_t)a.num_seqs * a.max_parts;
-  if (a.num_seqs <= kCompactSeqs) {
+  if (compact_plan(a)) {
     static const int per_cu = [] {
       int nb = 0;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, paged_decode_kernel<T, D, GT, F8, MODE>, kDecodeWaves * 64, 0) !=
