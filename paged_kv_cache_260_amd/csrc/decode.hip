@@ -910,6 +910,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
     if (tid < 16) mtot[tid] = tid < nmem ? mem_tot : 0;
   }
   __syncthreads();
+  // streaming runs at normal priority; the latency chains around it (plan,
+  // item start, merge) run raised, so a SIMD's streaming waves do not hold
+  // them up
+  __builtin_amdgcn_s_setprio(0);
   if constexpr (C::kPvMfma) {
     for (int ti = tb + wave; ti < te; ti += kNW) process(ti, rg, ti + kNW < te ? ti + kNW : -1);
   } else {
@@ -918,6 +922,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
       process(ti, rg, -1);
     }
   }
+  __builtin_amdgcn_s_setprio(2);
 
   // the next item's first loads fly while this one is merged and written
   if constexpr (kHead) {
@@ -1165,6 +1170,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT>()))) void paged
   // Larger batches take one item per workgroup in a fixed order:
   // partition-major, the sequence rotated by the partition so the partitions
   // of a long sequence spread over the chip.
+  __builtin_amdgcn_s_setprio(2);
   const int units = a.n_kv_heads * a.head_chunks;
   const int64_t lin = blockIdx.x;
   const int unit = (int)(lin % units);
