@@ -44,11 +44,12 @@ PROFILE_NAMES = {1: "paged_decode_tiny_f32_b4", 2: "paged_decode_mha_bf16_b64",
                  5: "paged_decode_prefix_f16_b64"}
 
 
-def measured_traffic(cfg, fused=True):
+def measured_traffic(cfg, fused=True, fp8=False):
     """HBM bytes per timed call from the committed counter summary of that step,
     or None when there is none or the decode source changed since the counters
     were taken."""
-    path = os.path.join(ROOT, "profiles", PROFILE_NAMES[cfg] + ("" if fused else "_two_call") + "_traffic.json")
+    name = PROFILE_NAMES[cfg] + ("_fp8" if fp8 else "") + ("" if fused else "_two_call")
+    path = os.path.join(ROOT, "profiles", name + "_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -480,7 +481,7 @@ def main():
         "logical_kv_bytes": int(logical_kv),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None if fp8 else measured_traffic(args.config, fused),
+                     "traffic": measured_traffic(args.config, fused, fp8),
                      "kernel": ("paged_attn_decode_append" if fused else "paged_attn_decode")
                                + " call (decode kernel"
                                + (")" if nparts == 1 else

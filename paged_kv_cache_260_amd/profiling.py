@@ -56,7 +56,8 @@ _DECODE_MODES = {"0": "", "1": " (chunk rows)", "2": " (shared prefix)", "3": " 
 
 
 def short_name(name: str) -> str:
-    for key in (*CALL_KERNELS, "paged_chunk_reduce_kernel", "paged_chunk_kernel", "kv_cache_write_kernel",
+    for key in (*CALL_KERNELS, "paged_chunk_reduce_kernel", "paged_chunk_kernel", "kv_cache_write_fp8_kernel",
+                "kv_cache_write_kernel",
                 "zero_i32_kernel", "copy_blocks_kernel", COPY_KERNEL):
         if key in name:
             if key == DECODE_KERNEL and name.endswith("EEEvNS_10DecodeArgsE") and "ELi" in name:
