@@ -304,7 +304,7 @@ def main():
                     help="decode = the hot-path step (default); copy_blocks = copy-on-write block copy")
     ap.add_argument("--step", default="append", choices=["append", "two-call"],
                     help="decode step: one call that appends the new token and decodes (default), or the "
-                         "cache write followed by the decode call (always so for FP8 pools)")
+                         "cache write followed by the decode call")
     ap.add_argument("--kv", default="native", choices=["native", "fp8"],
                     help="KV pool storage: the query dtype (default) or FP8 e4m3 codes with per-head scales")
     args = ap.parse_args()
@@ -369,15 +369,19 @@ def main():
 
     # 16-bit pools: one call appends the new token and decodes (the fused
     # step); --step two-call (and FP8 pools) time the write kernel, then decode
-    # (the one-call step is built for 16-bit pools; fp32 always takes two calls)
-    fused = args.step == "append" and not fp8 and w.dtype != torch.float32
+    # (the one-call step is built for 16-bit queries; fp32 always takes two calls)
+    fused = args.step == "append" and w.dtype != torch.float32
 
     def step(r, ev=None):
         if fused:
             if ev is not None:
                 ev[0].record(stream)
-            _lib.paged_attn_decode_append(out, q, kps[r], vps[r], kn, vn, bt, sl, w.scale, w.n_heads,
-                                          w.n_kv_heads, w.head_dim, w.block_size, stream=stream)
+            if fp8:
+                _lib.paged_attn_decode_append_fp8(out, q, kps[r], vps[r], kn, vn, ksd, vsd, bt, sl, w.scale,
+                                                  w.n_heads, w.n_kv_heads, w.head_dim, w.block_size, stream=stream)
+            else:
+                _lib.paged_attn_decode_append(out, q, kps[r], vps[r], kn, vn, bt, sl, w.scale, w.n_heads,
+                                              w.n_kv_heads, w.head_dim, w.block_size, stream=stream)
             if ev is not None:
                 ev[1].record(stream)
             return
@@ -468,8 +472,10 @@ def main():
             "cached_tokens": int(lens1.sum()), "mean_seq_len": round(float(lens1.mean()), 1),
             "max_seq_len": int(lens1.max()), "num_blocks": w.num_blocks,
             "partition_tokens": ptok, "max_partitions": nparts, "pool_replicas": R,
-            "step": ("paged_attn_decode_append: one call writes the new token (1 per seq) and decodes seq_len+1"
-                     if fused else "kv_cache_write (1 token/seq) + paged_attn_decode (seq_len+1)"),
+            "step": (f"paged_attn_decode_append{'_fp8' if fp8 else ''}: one call writes the new token (1 per seq) "
+                     f"and decodes seq_len+1" if fused else
+                     f"kv_cache_write{'_fp8' if fp8 else ''} (1 token/seq) + paged_attn_decode{'_fp8' if fp8 else ''} "
+                     f"(seq_len+1)"),
         },
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "us_per_batch": round(ms_step * 1e3, 3),
@@ -482,7 +488,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(args.config, fused, fp8),
-                     "kernel": ("paged_attn_decode_append" if fused else "paged_attn_decode")
+                     "kernel": ("paged_attn_decode_append" if fused else "paged_attn_decode") + ("_fp8" if fp8 else "")
                                + " call (decode kernel"
                                + (")" if nparts == 1 else
                                   ", partitions merged in-kernel)" if nparts <= FUSED_MERGE_PARTS else

@@ -66,6 +66,34 @@ PKV_API int pkv_kv_cache_write_fp8(void *k_pool, void *v_pool, const void *k_new
                                    int32_t num_tokens, int32_t n_kv_heads, int32_t head_dim,
                                    int32_t block_size, int64_t num_blocks, int32_t dtype, void *stream);
 
+/*
+ * pkv_paged_attn_decode_append over FP8 pools: one decode step in one launch.
+ * Equivalent to pkv_kv_cache_write_fp8 of k_new / v_new into the slot of
+ * position seq_lens[s] - 1 (slot = block_tables[s, (L - 1) / block_size] *
+ * block_size + (L - 1) % block_size) followed by pkv_paged_attn_decode_fp8
+ * with seq_lens, which here count the new token: the stored codes are those
+ * of the FP8 write, and the output equals the two calls' bit for bit. The
+ * work item that holds a sequence's newest token encodes and stores its rows
+ * and attends over their decoded codes from on-chip memory (engine step on
+ * the vLLM notes page: slots first, then the pass that writes the new K/V and
+ * attends; KV quantization as a KV-cache optimisation on the vLLM paper page).
+ *
+ * Arguments: as in pkv_paged_attn_decode_fp8, plus
+ *   k_pool, v_pool   read and written (uint8 e4m3 codes; the new rows are stored)
+ *   k_new, v_new     read, [num_seqs, n_kv_heads, head_dim] of dtype, 16-byte aligned
+ *   seq_lens         read, tokens per sequence including the new one (0 = empty
+ *                    sequence: zero output, nothing written)
+ *   dtype            of q, out, k_new and v_new: PKV_F16 or PKV_BF16
+ * A sequence with an invalid length or table entry gets NaN rows and no write.
+ */
+PKV_API int pkv_paged_attn_decode_append_fp8(void *out, const void *q, void *k_pool, void *v_pool,
+                                             const void *k_new, const void *v_new, const float *k_scale,
+                                             const float *v_scale, const int32_t *block_tables,
+                                             const int32_t *seq_lens, float scale, int32_t n_heads,
+                                             int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                                             int32_t num_seqs, int32_t max_blocks_per_seq, int64_t num_blocks,
+                                             int32_t dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

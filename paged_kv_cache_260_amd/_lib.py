@@ -70,6 +70,8 @@ _SIGNATURES = {
                                                  _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
     "pkv_kv_cache_write_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                               _i64, _i32, _vp]),
+    "pkv_paged_attn_decode_append_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32,
+                                                        _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
 }
 
 
@@ -542,4 +544,40 @@ def paged_attn_decode_append(out, q, k_pool, v_pool, k_new, v_new, block_tables,
             out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
             block_tables.data_ptr(), seq_lens.data_ptr(), float(scale), n_heads, n_kv_heads, head_dim, block_size,
             B, block_tables.shape[1], k_pool.shape[0], DTYPE_CODES[dt], _stream_handle(q, stream)))
+    return out
+
+
+def paged_attn_decode_append_fp8(out, q, k_pool, v_pool, k_new, v_new, k_scale, v_scale, block_tables, seq_lens,
+                                 scale: float, n_heads: int, n_kv_heads: int, head_dim: int, block_size: int,
+                                 stream=None):
+    """One decode step over FP8 pools (uint8 e4m3 codes ``[NB, Hkv, BS, D]``,
+    float32 scales ``[Hkv]``): encode and store each sequence's newest token
+    (``k_new``/``v_new`` ``[B, Hkv, D]`` in the query dtype) at position
+    ``seq_lens - 1`` of its table, then decode over ``seq_lens`` tokens."""
+    dt = q.dtype
+    _need(dt in (torch.float16, torch.bfloat16), f"FP8 pools need an fp16/bf16 query, got {dt}")
+    for name, t in (("out", out), ("q", q), ("k_new", k_new), ("v_new", v_new)):
+        _dev_tensor(t, name, dt)
+    for name, t in (("k_pool", k_pool), ("v_pool", v_pool)):
+        _dev_tensor(t, name, torch.uint8)
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        _dev_tensor(t, name, torch.float32)
+        _need(t.shape == (n_kv_heads,), f"{name} must be [Hkv]")
+    for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens)):
+        _dev_tensor(t, name, torch.int32)
+    B = seq_lens.shape[0]
+    _need(q.shape == (B, n_heads, head_dim) and out.shape == q.shape, "q/out must be [B, H, D]")
+    _need(k_new.shape == (B, n_kv_heads, head_dim) and v_new.shape == k_new.shape, "k_new/v_new must be [B, Hkv, D]")
+    _need(k_pool.dim() == 4 and k_pool.shape[1:] == (n_kv_heads, block_size, head_dim),
+          "k_pool must be [NB, Hkv, BS, D]")
+    _need(v_pool.shape == k_pool.shape, "v_pool must match k_pool")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B, MB]")
+    devs = {t.device for t in (out, q, k_pool, v_pool, k_new, v_new, k_scale, v_scale, block_tables, seq_lens)}
+    _need(len(devs) == 1, "all tensors must be on one device")
+    with torch.cuda.device(q.device):
+        _check(lib().pkv_paged_attn_decode_append_fp8(
+            out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+            k_scale.data_ptr(), v_scale.data_ptr(), block_tables.data_ptr(), seq_lens.data_ptr(), float(scale),
+            n_heads, n_kv_heads, head_dim, block_size, B, block_tables.shape[1], k_pool.shape[0], DTYPE_CODES[dt],
+            _stream_handle(q, stream)))
     return out

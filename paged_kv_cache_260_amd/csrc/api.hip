@@ -282,7 +282,7 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
       if (rc != PKV_OK) return rc;
     }
   }
-  hipError_t e = append ? pkv::launch_decode_append(static_cast<pkv::DType>(dtype), head_dim, a, st)
+  hipError_t e = append ? pkv::launch_decode_append(static_cast<pkv::DType>(dtype), head_dim, fp8, a, st)
                  : fp8  ? pkv::launch_decode_fp8(static_cast<pkv::DType>(dtype), head_dim, a, st)
                         : pkv::launch_decode(static_cast<pkv::DType>(dtype), head_dim, a, st);
   if (e != hipSuccess) return hip_fail(e, "paged decode launch");
@@ -310,6 +310,17 @@ int pkv_paged_attn_decode_append(void *out, const void *q, void *k_pool, void *v
                                  int64_t num_blocks, int32_t dtype, void *stream) {
   return decode_impl(out, q, k_pool, v_pool, block_tables, seq_lens, scale, n_heads, n_kv_heads, head_dim,
                      block_size, num_seqs, max_blocks_per_seq, num_blocks, dtype, stream, false, nullptr, nullptr,
+                     k_new, v_new);
+}
+
+int pkv_paged_attn_decode_append_fp8(void *out, const void *q, void *k_pool, void *v_pool, const void *k_new,
+                                     const void *v_new, const float *k_scale, const float *v_scale,
+                                     const int32_t *block_tables, const int32_t *seq_lens, float scale,
+                                     int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                                     int32_t num_seqs, int32_t max_blocks_per_seq, int64_t num_blocks,
+                                     int32_t dtype, void *stream) {
+  return decode_impl(out, q, k_pool, v_pool, block_tables, seq_lens, scale, n_heads, n_kv_heads, head_dim,
+                     block_size, num_seqs, max_blocks_per_seq, num_blocks, dtype, stream, true, k_scale, v_scale,
                      k_new, v_new);
 }
 

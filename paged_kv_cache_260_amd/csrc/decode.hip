@@ -37,6 +37,7 @@
 //      transposed with ds_read_b64_tr_b16 and multiplied on
 //      v_mfma_f32_16x16x16; fp32 storage accumulates P * V on the VALU.
 #include "attn_common.h"
+#include "fp8_encode.h"
 #include "kernels.h"
 
 #include <math.h>
@@ -398,7 +399,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   static_assert(!F8 || C::kPvMfma, "FP8 pools need a 16-bit query type");
   static_assert(!RM || (GT == 16 && C::kPvMfma), "chunk rows: 16-row tiles, 16-bit types");
   static_assert(MODE != kModeSuffix || C::kPvMfma, "shared-prefix decode: 16-bit types");
-  static_assert(MODE != kModeAppend || (C::kPvMfma && !F8), "append: 16-bit pools");
+  static_assert(MODE != kModeAppend || C::kPvMfma, "append: 16-bit queries");
   constexpr int kKvBytes = F8 ? 1 : (int)sizeof(T);     // bytes per stored element
   constexpr int kL = kTileTokens * D * kKvBytes / (16 * 64);  // 16-byte loads per lane per K (or V) tile
   constexpr int kChKV = D * kKvBytes / 16;               // 16-byte chunks per stored token row
@@ -897,9 +898,33 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   // the pool copy (head chunk 0 only, at the slot the table gives) is stored
   // after the tile loop, so no wait on it sits in front of the K/V loads
   int new_phys = -1;
+  uint2 new_codes = make_uint2(0u, 0u);  // FP8 pools: this thread's 8 codes of the new row
   if constexpr (MODE == kModeAppend) {
     if (holds_new) {
-      if (tid < 2 * kCh) reinterpret_cast<u32x4_t *>(smem + C::kNewOff)[tid] = new_chunk;
+      u32x4_t staged = new_chunk;
+      if constexpr (F8) {
+        // encode as the FP8 cache write does (x * (1 / scale), nearest e4m3),
+        // and stage the codes decoded exactly, as a tile load of the written
+        // slot would
+        if (tid < 2 * kCh) {
+          const float inv = __fdiv_rn(1.0f, (tid < kCh ? a.k_scale : a.v_scale)[g]);
+          const T *e = reinterpret_cast<const T *>(&new_chunk);
+          uint32_t w[2] = {0u, 0u};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) w[j >> 2] |= f32_to_e4m3(__fmul_rn(static_cast<float>(e[j]), inv)) << (8 * (j & 3));
+          new_codes = make_uint2(w[0], w[1]);
+          uint32_t d[4];
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+            const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+            d[2 * i] = pack2_exact<T>(f01[0], f01[1]);
+            d[2 * i + 1] = pack2_exact<T>(f23[0], f23[1]);
+          }
+          staged = u32x4_t{d[0], d[1], d[2], d[3]};
+        }
+      }
+      if (tid < 2 * kCh) reinterpret_cast<u32x4_t *>(smem + C::kNewOff)[tid] = staged;
       const int phys = __builtin_amdgcn_readlane(btv, (tok_new >> a.block_shift) - jb);
       if (hc == 0 && phys >= 0 && (int64_t)phys < a.num_blocks) new_phys = phys;
     }
@@ -934,9 +959,16 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   }
   if constexpr (MODE == kModeAppend) {
     if (new_phys >= 0 && tid < 2 * kCh) {
-      u32x4_t *dst = static_cast<u32x4_t *>(const_cast<void *>(tid < kCh ? a.k_pool : a.v_pool));
-      dst[((int64_t)new_phys * kv_stride_blk + (int64_t)g * a.block_size + (tok_new & (a.block_size - 1))) * kCh +
-          (tid % kCh)] = reinterpret_cast<const u32x4_t *>(smem + C::kNewOff)[tid];
+      const int64_t row = (int64_t)new_phys * kv_stride_blk + (int64_t)g * a.block_size + (tok_new & (a.block_size - 1));
+      if constexpr (F8) {
+        // D codes per row: this thread's 8 at byte (tid % kCh) * 8
+        uint2 *dst = reinterpret_cast<uint2 *>(static_cast<uint8_t *>(const_cast<void *>(tid < kCh ? a.k_pool : a.v_pool)) +
+                                               row * D) + (tid % kCh);
+        *dst = new_codes;
+      } else {
+        u32x4_t *dst = static_cast<u32x4_t *>(const_cast<void *>(tid < kCh ? a.k_pool : a.v_pool));
+        dst[row * kCh + (tid % kCh)] = reinterpret_cast<const u32x4_t *>(smem + C::kNewOff)[tid];
+      }
     }
   }
 
@@ -1150,13 +1182,17 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
 // Three workgroups per CU (12 waves) keep enough K/V loads in flight; the
 // register budget is pinned so the item loop does not trade occupancy for
 // registers. fp32 storage with large head tiles needs more registers.
-template <typename T, int D, int GT> constexpr int decode_waves_per_eu() {
-  return (sizeof(T) == 2 || GT <= 4) ? 3 : 2;
+// Waves per SIMD the register budget is set for: 16-bit pools 3 (at 4 the
+// tile loop no longer fits its registers and runs much slower), FP8 pools 4
+// (half the bytes per tile, so more waves keep more bytes in flight; their
+// LDS fits 4 workgroups per CU).
+template <typename T, int D, int GT, bool F8> constexpr int decode_waves_per_eu() {
+  return F8 ? 4 : (sizeof(T) == 2 || GT <= 4) ? 3 : 2;
 }
 
 template <typename T, int D, int GT, bool F8, int MODE>
 __global__ __launch_bounds__(kDecodeWaves * 64)
-__attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT>()))) void paged_decode_kernel(DecodeArgs a) {
+__attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT, F8>()))) void paged_decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[Cfg<T, D, GT>::kSmem];
   // Work items. The hardware deals workgroup i to XCD i % 8, and workgroups
   // start in index order as slots free up. The unit (KV head x query-head
@@ -1639,32 +1675,36 @@ hipError_t launch_shared_fused(DType dt, int head_dim, bool fp8, const DecodeArg
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool F8>
 hipError_t launch_append_td(int gt, const DecodeArgs &a, hipStream_t stream) {
   switch (gt) {
-    case 1: return launch_t<T, D, 1, false, kModeAppend>(a, stream);
-    case 2: return launch_t<T, D, 2, false, kModeAppend>(a, stream);
-    case 4: return launch_t<T, D, 4, false, kModeAppend>(a, stream);
-    case 8: return launch_t<T, D, 8, false, kModeAppend>(a, stream);
-    case 16: return launch_t<T, D, 16, false, kModeAppend>(a, stream);
+    case 1: return launch_t<T, D, 1, F8, kModeAppend>(a, stream);
+    case 2: return launch_t<T, D, 2, F8, kModeAppend>(a, stream);
+    case 4: return launch_t<T, D, 4, F8, kModeAppend>(a, stream);
+    case 8: return launch_t<T, D, 8, F8, kModeAppend>(a, stream);
+    case 16: return launch_t<T, D, 16, F8, kModeAppend>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename T>
+template <typename T, bool F8>
 hipError_t launch_append_t(int head_dim, int gt, const DecodeArgs &a, hipStream_t stream) {
   switch (head_dim) {
-    case 64: return launch_append_td<T, 64>(gt, a, stream);
-    case 128: return launch_append_td<T, 128>(gt, a, stream);
+    case 64: return launch_append_td<T, 64, F8>(gt, a, stream);
+    case 128: return launch_append_td<T, 128, F8>(gt, a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_decode_append(DType dt, int head_dim, const DecodeArgs &a, hipStream_t stream) {
+hipError_t launch_decode_append(DType dt, int head_dim, bool fp8, const DecodeArgs &a, hipStream_t stream) {
   const int gt = decode_head_tile(a.group);
   switch (dt) {
-    case DType::F16: return launch_append_t<_Float16>(head_dim, gt, a, stream);
-    case DType::BF16: return launch_append_t<__bf16>(head_dim, gt, a, stream);
+    case DType::F16:
+      return fp8 ? launch_append_t<_Float16, true>(head_dim, gt, a, stream)
+                 : launch_append_t<_Float16, false>(head_dim, gt, a, stream);
+    case DType::BF16:
+      return fp8 ? launch_append_t<__bf16, true>(head_dim, gt, a, stream)
+                 : launch_append_t<__bf16, false>(head_dim, gt, a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -71,7 +71,8 @@ struct DecodeArgs {
   int32_t prefix_partition_tokens;  // the shortest allowed (the kernel may lengthen it)
   int32_t prefix_partition_fixed;   // nonzero: use prefix_partition_tokens as given
   // Decode with append (launch_decode_append): the newest token's K and V
-  // rows, [num_seqs, n_kv_heads, head_dim] of the pool type
+  // rows, [num_seqs, n_kv_heads, head_dim] of the query type (FP8 pools:
+  // encoded with k_scale / v_scale on their way in)
   const void *k_new;
   const void *v_new;
 };
@@ -139,8 +140,9 @@ hipError_t launch_shared_prefix(DType dt, int head_dim, bool fp8, const DecodeAr
 hipError_t launch_shared_fused(DType dt, int head_dim, bool fp8, const DecodeArgs &a, hipStream_t stream);
 
 // Decode that first appends each sequence's newest token (position
-// seq_lens[s] - 1) from a.k_new / a.v_new into its slot; dt is F16 or BF16.
-hipError_t launch_decode_append(DType dt, int head_dim, const DecodeArgs &a, hipStream_t stream);
+// seq_lens[s] - 1) from a.k_new / a.v_new into its slot; dt is F16 or BF16;
+// fp8: the pools hold e4m3 codes (a.k_scale / a.v_scale).
+hipError_t launch_decode_append(DType dt, int head_dim, bool fp8, const DecodeArgs &a, hipStream_t stream);
 
 // Same over FP8 (OCP e4m3) pools with a.k_scale / a.v_scale; dt (query and
 // output) must be F16 or BF16.

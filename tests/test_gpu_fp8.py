@@ -162,6 +162,44 @@ def test_fp8_write_then_decode():
     assert max_abs_err(out, oracle_fp8(w, k_ref, v_ref, ks, vs, seq_lens=lens)) <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("partition", [0, 128])
+@pytest.mark.parametrize("D,BS,H,Hkv,dtype,seed", [(128, 16, 32, 8, torch.bfloat16, 11),
+                                                   (64, 32, 8, 8, torch.float16, 12)])
+def test_fp8_append_one_call(D, BS, H, Hkv, dtype, seed, partition):
+    """The one-call step over FP8 pools: the pools equal the oracle's quantizing
+    write byte for byte, the output is within the tolerance of the oracle on
+    those pools, and bit-identical to the quantizing write followed by FP8
+    decode. The new token's slot holds the poison NaN code before the call, so
+    the kernel must attend over the new rows, not over what the slot held."""
+    _lib.set_partition_tokens(partition)
+    w = workloads.random_case(seed, num_seqs=9, n_heads=H, n_kv_heads=Hkv, head_dim=D, block_size=BS,
+                              dtype=dtype, max_len=1800, poison=True)
+    say(f"fp8 append: D={D} BS={BS} H={H} Hkv={Hkv} {dtype} partition={partition} lens={list(w.seq_lens)}")
+    kc, vc, ks, vs = fp8_case(w, seed)
+    dev = "cuda"
+    lens = w.seq_lens_after_write()
+    q = w.q.to(dev)
+    ksd, vsd = torch.from_numpy(ks).to(dev), torch.from_numpy(vs).to(dev)
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    lensd = torch.from_numpy(lens).to(dev)
+    kn, vn = w.k_new.to(dev), w.v_new.to(dev)
+    kp1, vp1 = torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev)
+    out1 = torch.empty_like(q)
+    _lib.paged_attn_decode_append_fp8(out1, q, kp1, vp1, kn, vn, ksd, vsd, bt, lensd, w.scale, w.n_heads,
+                                      w.n_kv_heads, w.head_dim, w.block_size)
+    kp2, vp2 = torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev)
+    out2 = torch.empty_like(q)
+    _lib.kv_cache_write_fp8(kp2, vp2, kn, vn, ksd, vsd, torch.from_numpy(w.slot_mapping).to(dev))
+    _lib.paged_attn_decode_fp8(out2, q, kp2, vp2, ksd, vsd, bt, lensd, w.scale, w.n_heads, w.n_kv_heads,
+                               w.head_dim, w.block_size)
+    torch.cuda.synchronize()
+    k_ref, v_ref = ofp8.kv_cache_write_fp8(kc, vc, f32np(w.k_new), f32np(w.v_new), ks, vs, w.slot_mapping,
+                                           w.block_size)
+    assert np.array_equal(kp1.cpu().numpy(), k_ref) and np.array_equal(vp1.cpu().numpy(), v_ref)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16)), "one call differs from write + decode"
+    assert max_abs_err(out1, oracle_fp8(w, k_ref, v_ref, ks, vs, seq_lens=lens)) <= TOL[w.dtype]
+
+
 def test_fp8_copy_blocks_bit_exact():
     rng = np.random.default_rng(3)
     k = rng.integers(0, 256, size=(50, 8, 16, 128), dtype=np.uint8)
