@@ -269,18 +269,24 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
     return fail(PKV_ERR_INVALID, "%d sequences x %d partitions x %d heads: too many workgroups",
                 num_seqs, a.max_parts, n_kv_heads);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // counters, one buffer per (device, stream): the ticket counter of the
+  // late workgroups first, then (in-kernel merge) the arrival counters
+  constexpr int64_t kTicketInts = 64;
+  const bool fused_merge = a.max_parts > 1 && a.max_parts <= pkv::kFusedMergeParts;
+  int32_t *counters = nullptr;
+  int rc = get_arrivals(st, kTicketInts + (fused_merge ? (int64_t)num_seqs * n_kv_heads * a.head_chunks : 0),
+                        &counters);
+  if (rc != PKV_OK) return rc;
+  a.tickets = reinterpret_cast<uint32_t *>(counters);
   if (a.max_parts > 1) {
     const size_t rows = (size_t)num_seqs * n_heads * a.max_parts;
     const size_t acc_bytes = rows * head_dim * sizeof(float);
     void *ws = nullptr;
-    int rc = get_workspace(st, acc_bytes + rows * sizeof(float2), &ws);
+    rc = get_workspace(st, acc_bytes + rows * sizeof(float2), &ws);
     if (rc != PKV_OK) return rc;
     a.part_acc = static_cast<float *>(ws);
     a.part_ml = reinterpret_cast<float2 *>(static_cast<char *>(ws) + acc_bytes);
-    if (a.max_parts <= pkv::kFusedMergeParts) {
-      rc = get_arrivals(st, (int64_t)num_seqs * n_kv_heads * a.head_chunks, &a.arrivals);
-      if (rc != PKV_OK) return rc;
-    }
+    if (fused_merge) a.arrivals = counters + kTicketInts;
   }
   hipError_t e = append ? pkv::launch_decode_append(static_cast<pkv::DType>(dtype), head_dim, fp8, a, st)
                  : fp8  ? pkv::launch_decode_fp8(static_cast<pkv::DType>(dtype), head_dim, a, st)

@@ -42,6 +42,7 @@
 
 #include <math.h>
 
+#include <algorithm>
 #include <atomic>
 
 namespace pkv {
@@ -68,7 +69,8 @@ constexpr int kRemBuckets = 8;
 constexpr int kPlanEntry = 0;
 constexpr int kPlanCnt = kCompactSeqs;
 constexpr int kPlanAux = kPlanCnt + (kRemBuckets + 1) * kCompactChunks + kCompactChunks;
-constexpr int kPlanInts = kPlanAux + kCompactChunks;
+constexpr int kPlanTicket = kPlanAux + kCompactChunks;  // a late workgroup's ticket
+constexpr int kPlanInts = kPlanTicket + 1;
 static_assert(kDecodeWaves == kCompactChunks, "one wave per 64-entity chunk of the plan");
 static_assert((kRemBuckets + 1) * kCompactChunks <= 64, "bucket counts fit one wave");
 static_assert(kCompactSeqs <= 256, "remainder ranks take 8 bits of a plan entry");
@@ -197,7 +199,8 @@ __device__ __forceinline__ int shared_prefix_partition(const DecodeArgs &a, int 
 // [64 c, 64 c + 64) (one load round trip), counts them per bucket, and after
 // one barrier every wave turns the chunk counts into positions; a second
 // barrier publishes them. Every workgroup computes the same plan.
-template <int MODE> __device__ __forceinline__ void make_plan(const DecodeArgs &a, ItemPlan &pl, int *sp) {
+template <int MODE>
+__device__ __forceinline__ void make_plan(const DecodeArgs &a, ItemPlan &pl, int *sp, bool claim, uint32_t ticket) {
   const int lane = threadIdx.x & 63;
   const int c = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // this wave's chunk
   const int e = c * 64 + lane;                                            // this lane's entity
@@ -256,6 +259,8 @@ template <int MODE> __device__ __forceinline__ void make_plan(const DecodeArgs &
   }
   if (lane <= kRemBuckets) sp[kPlanCnt + lane * kCompactChunks + c] = my_cnt;
   if (lane == 63) sp[kPlanCnt + (kRemBuckets + 1) * kCompactChunks + c] = x;
+  // thread 0's ticket (its atomic returned with the lengths) for the workgroup
+  if (claim && threadIdx.x == 0) sp[kPlanTicket] = (int)ticket;
   __syncthreads();
   // exclusive prefix over (bucket, chunk), bucket-major: the remainder list
   // takes bucket 0 of every chunk in chunk order, then bucket 1, ...
@@ -1208,19 +1213,39 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT, F8>()))) void p
   // of a long sequence spread over the chip.
   __builtin_amdgcn_s_setprio(2);
   const int units = a.n_kv_heads * a.head_chunks;
-  const int64_t lin = blockIdx.x;
-  const int unit = (int)(lin % units);
-  const int w = (int)(lin / units);
   const bool compact = compact_plan(a);
+  // A workgroup past the first static_wgs takes the place of workgroup
+  // static_wgs + ticket: the claimers together cover exactly those places,
+  // in the order their slots free up on any XCD (the counter wraps to zero
+  // after the last of the gridDim - static_wgs tickets). The fixed map sends
+  // workgroup i to XCD i mod 8, and XCDs finish their equal shares several
+  // microseconds apart; tickets let the later, shorter items go to the XCDs
+  // that are ahead.
+  const bool claim = compact && a.tickets != nullptr && (int64_t)blockIdx.x >= a.static_wgs;
+  uint32_t ticket = 0;
+  if (claim && threadIdx.x == 0)
+    ticket = __builtin_amdgcn_atomic_inc32(a.tickets, gridDim.x - (uint32_t)a.static_wgs - 1u, __ATOMIC_RELAXED,
+                                           "agent");
   ItemPlan plan;
   plan.p_pre = a.prefix_partition_tokens;
   plan.full_items = plan.items = 0;
   int *plan_lds = reinterpret_cast<int *>(smem + Cfg<T, D, GT>::kPlanOff);
-  if (compact) make_plan<MODE>(a, plan, plan_lds);
+  if (compact) make_plan<MODE>(a, plan, plan_lds, claim, ticket);
+  // Tickets place items only when every workgroup takes one item (a unit has
+  // no more items than workgroups); with two or more rounds per workgroup the
+  // fixed places measured faster. Every claimer has drawn its ticket either
+  // way, so the counter still wraps to zero.
+  const bool placed = claim && plan.items <= a.wgs_per_unit;
+  const int64_t lin = placed ? (int64_t)a.static_wgs + __builtin_amdgcn_readfirstlane(plan_lds[kPlanTicket])
+                             : (int64_t)blockIdx.x;
+  const int unit = (int)(lin % units);
+  const int w = (int)(lin / units);
   ItemHead<Cfg<T, D, GT>::kQPer> hd{};
   hd.ready = false;
   // item j of this workgroup's walk (compact plans), or -1 past its end
+  const bool lin_ok = lin < (int64_t)gridDim.x;  // a ticket past the call's range (never, with a clean counter)
   auto item_of = [&](int round) -> int64_t {
+    if (!lin_ok) return -1;
     const int G = a.wgs_per_unit;
     const int64_t j = (int64_t)round * G + ((round & 1) ? G - 1 - w : w);
     return j < plan.items ? j : -1;
@@ -1522,12 +1547,23 @@ hipError_t launch_t(const DecodeArgs &args, hipStream_t stream) {
         nb = 1;
       return nb;
     }();
-    const int64_t slots = (int64_t)per_cu * device_cus() * kWgsPerSlot;
+    const int64_t resident = (int64_t)per_cu * device_cus();
+    const int64_t slots = resident * kWgsPerSlot;
     int64_t g = (slots + units - 1) / units;
+    // Tickets (the first `resident` workgroups keep their places, the rest
+    // claim theirs) pay off when most workgroups take a single item: measured
+    // on batches with more workgroups per unit than sequences and at least 32
+    // sequences (GQA batch 128: -1.6 us); with fewer workgroups per unit
+    // (MHA batch 64) or few long sequences (4 x 32K-128K), where workgroups
+    // take two or more items, the claims cost 0.5-1% and tickets stay off.
+    if (g <= a.num_seqs || a.num_seqs < 32) a.tickets = nullptr;
     if (g < a.num_seqs) g = a.num_seqs;
     a.wgs_per_unit = (int32_t)(g < max_items ? g : max_items);
+    a.static_wgs = (int32_t)std::min<int64_t>(resident, units * a.wgs_per_unit);
+    if (a.static_wgs >= units * a.wgs_per_unit) a.tickets = nullptr;
   } else {
     a.wgs_per_unit = (int32_t)max_items;
+    a.tickets = nullptr;
   }
   dim3 grid((unsigned)(units * a.wgs_per_unit), 1, 1);
   hipLaunchKernelGGL((paged_decode_kernel<T, D, GT, F8, MODE>), grid, dim3(kDecodeWaves * 64), 0, stream, a);

@@ -44,6 +44,12 @@ struct DecodeArgs {
   // set when the partitions of a sequence are merged by the last of them to
   // finish (max_parts <= kFusedMergeParts), null when a merge kernel runs.
   int32_t *arrivals;
+  // Longest-first plans: workgroups past the first static_wgs (those the chip
+  // starts at once) take their place in the order from a ticket counter, so
+  // the later items go to whichever XCD frees a slot first. The counter wraps
+  // to zero after the call's last ticket (null: fixed places).
+  uint32_t *tickets;
+  int32_t static_wgs;      // set by the launch
   // FP8 pools only: per-KV-head scales of the stored codes (null otherwise)
   const float *k_scale;
   const float *v_scale;
