@@ -1556,7 +1556,9 @@ hipError_t launch_t(const DecodeArgs &args, hipStream_t stream) {
     // sequences (GQA batch 128: -1.6 us); with fewer workgroups per unit
     // (MHA batch 64) or few long sequences (4 x 32K-128K), where workgroups
     // take two or more items, the claims cost 0.5-1% and tickets stay off.
-    if (g <= a.num_seqs || a.num_seqs < 32) a.tickets = nullptr;
+    // FP8 pools (4 workgroups per CU, half the bytes per item) measured
+    // slower with tickets (GQA batch 128: 40.2 -> 43.0 us): off as well.
+    if (F8 || g <= a.num_seqs || a.num_seqs < 32) a.tickets = nullptr;
     if (g < a.num_seqs) g = a.num_seqs;
     a.wgs_per_unit = (int32_t)(g < max_items ? g : max_items);
     a.static_wgs = (int32_t)std::min<int64_t>(resident, units * a.wgs_per_unit);
