@@ -403,18 +403,23 @@ int chunk_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
     plan(block_size, max_blocks_per_seq, &a.partition_tokens, &a.max_parts);
     const int64_t items = (int64_t)num_seqs * n_kv_heads * row_blocks;
     if (items * a.max_parts > (int64_t)INT32_MAX) return fail(PKV_ERR_INVALID, "too many work items");
+    // the late workgroups' ticket counter first, then the arrival counters
+    // (as in decode)
+    constexpr int64_t kTicketInts = 64;
+    const bool fused_merge = a.max_parts > 1 && a.max_parts <= pkv::kFusedMergeParts;
+    int32_t *counters = nullptr;
+    int rc = get_arrivals(st, kTicketInts + (fused_merge ? items : 0), &counters);
+    if (rc != PKV_OK) return rc;
+    a.tickets = reinterpret_cast<uint32_t *>(counters);
     if (a.max_parts > 1) {
       const size_t rows = (size_t)items * 16 * a.max_parts;
       const size_t acc_bytes = rows * head_dim * sizeof(float);
       void *ws = nullptr;
-      int rc = get_workspace(st, acc_bytes + rows * sizeof(float2), &ws);
+      rc = get_workspace(st, acc_bytes + rows * sizeof(float2), &ws);
       if (rc != PKV_OK) return rc;
       a.part_acc = static_cast<float *>(ws);
       a.part_ml = reinterpret_cast<float2 *>(static_cast<char *>(ws) + acc_bytes);
-      if (a.max_parts <= pkv::kFusedMergeParts) {
-        rc = get_arrivals(st, items, &a.arrivals);
-        if (rc != PKV_OK) return rc;
-      }
+      if (fused_merge) a.arrivals = counters + kTicketInts;
     }
     hipError_t e = pkv::launch_chunk_rows(static_cast<pkv::DType>(dtype), head_dim, fp8, a, st);
     if (e != hipSuccess) return hip_fail(e, "chunk attention launch");
