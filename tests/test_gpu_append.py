@@ -134,3 +134,23 @@ def test_append_invalid_length_gives_nan_and_no_write():
     for s in (0, 1, 3):
         blk, off = divmod(int(w.slot_mapping[s]), w.block_size)
         assert torch.equal(kp[blk, :, off].cpu().view(torch.int16), w.k_new[s].view(torch.int16))
+
+
+def test_ticket_placement_repeats_across_grids():
+    """Late workgroups take their places from a counter that must be back at
+    zero after every call. Calls with three different grids in a row (batch
+    128, 40, 128 again; the later workgroups of the 128-sequence batches claim
+    places, the 40-sequence batch has its own claimer count): each output is
+    bit-identical to the two-call path, and the repeated batch gives the same
+    bits as its first call."""
+    ws = [workloads.random_case(700 + b, num_seqs=b, n_heads=32, n_kv_heads=8, head_dim=128, block_size=16,
+                                dtype=torch.bfloat16, max_len=1500, min_len=16, poison=True) for b in (128, 40)]
+    outs = []
+    for w in (ws[0], ws[1], ws[0]):
+        say(f"tickets: batch {w.num_seqs}")
+        lens = w.seq_lens_after_write()
+        out, _, _ = run_append(w, lens)
+        out2, _, _ = run_two_calls(w, lens)
+        assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.int16), outs[2].view(torch.int16))
