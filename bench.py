@@ -45,19 +45,21 @@ PROFILE_NAMES = {1: "paged_decode_tiny_f32_b4", 2: "paged_decode_mha_bf16_b64",
 
 
 def measured_traffic(cfg, fused=True, fp8=False):
-    """HBM bytes per timed call from the committed counter summary of that step,
-    or None when there is none or the decode source changed since the counters
-    were taken."""
+    """(HBM bytes per timed call, where they come from): read back from the
+    committed FETCH_SIZE/WRITE_SIZE summary of that step under profiles/, not
+    measured in this run; (None, reason) when there is none or the decode
+    source changed since the counters were taken."""
     name = PROFILE_NAMES[cfg] + ("_fp8" if fp8 else "") + ("" if fused else "_two_call")
-    path = os.path.join(ROOT, "profiles", name + "_traffic.json")
+    rel = os.path.join("profiles", name + "_traffic.json")
     try:
-        with open(path) as f:
+        with open(os.path.join(ROOT, rel)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
-        return None
-    if rec.get("decode_source_hash") != profiling.source_hash() or "traffic_bytes_per_call" not in rec:
-        return None
-    return int(rec["traffic_bytes_per_call"])
+        return None, f"no counter summary ({rel})"
+    src = profiling.source_hash()
+    if rec.get("decode_source_hash") != src or "traffic_bytes_per_call" not in rec:
+        return None, f"{rel} was taken on decode source {rec.get('decode_source_hash')}, not {src}"
+    return int(rec["traffic_bytes_per_call"]), f"from {rel} @ decode source {src} (rocprofv3 counters, earlier run)"
 
 
 def log(msg):
@@ -65,27 +67,41 @@ def log(msg):
 
 
 def stream_ceiling(device, nbytes=2 * 2 ** 30, iters=10):
-    """torch's own reduction and copy over a 2 GiB buffer: a measured read ceiling."""
-    x = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=device).normal_()
-    y = torch.empty_like(x)
-    for _ in range(2):
-        x.sum()
-        y.copy_(x)
-    torch.cuda.synchronize()
-    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-    e0.record()
-    for _ in range(iters):
-        x.sum()
-    e1.record()
-    for _ in range(iters):
-        y.copy_(x)
-    e2.record()
-    torch.cuda.synchronize()
-    read = nbytes * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    copy = 2 * nbytes * iters / (e1.elapsed_time(e2) * 1e-3) / 1e9
-    del x, y
+    """Measured read ceilings (the library's probe kernels, pkv_probe.h) over
+    a 2 GiB buffer, 8x the memory-side cache: a sequential non-temporal read,
+    and a gather of 4 KiB tiles in shuffled order (the decode kernel's
+    pattern: one tile = one 16-token block of one KV head) at 1, 2 and 4 tiles
+    in flight per wave and two grid sizes; the best gather is reported with its
+    configuration. HIP events on the stream the probes run on."""
+    stream = torch.cuda.current_stream(device)
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device=device).random_()
+    cus = torch.cuda.get_device_properties(device).multi_processor_count
+    sink = torch.zeros(64 * cus, dtype=torch.int32, device=device)
+    tiles = torch.randperm(nbytes // 4096, device=device).to(torch.int32)
+
+    def timed(run):
+        run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return nbytes * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+    res = {"stream_read": round(timed(lambda: _lib.probe_stream_read(buf, 8 * cus, sink, stream=stream)), 1)}
+    best = (0.0, None)
+    for depth in (1, 2, 4):
+        for per_cu in (8, 16):
+            g = timed(lambda: _lib.probe_gather_tiles(buf, tiles, depth, per_cu * cus, sink, stream=stream))
+            if g > best[0]:
+                best = (g, f"{depth} tiles in flight per wave, {per_cu} workgroups of 4 waves per CU")
+    res["gather_4k_tiles"] = round(best[0], 1)
+    res["gather_config"] = best[1]
+    res["buffer_bytes"] = nbytes
+    del buf, tiles, sink
     torch.cuda.empty_cache()
-    return read, copy
+    return res
 
 
 def cpu_baseline(w, lens_after, kp_after, vp_after, budget_s, fp8_scales=None):
@@ -297,6 +313,8 @@ def main():
                     help="workload (3 = GQA bf16 batch 128, the headline)")
     ap.add_argument("--replicas", type=int, default=0, help="pool copies to rotate (0 = auto)")
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = automatic)")
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="after the warm-up steps, keep stepping (untimed) until this much wall time has passed")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
@@ -404,6 +422,17 @@ def main():
     for i in range(args.warmup):
         step(i % R)
     torch.cuda.synchronize()
+    # The GPU clocks take tens of milliseconds of steady work to settle (a run
+    # timed after a few warm-up steps reads about 1.5 us per call slow): keep
+    # stepping, untimed, until --settle-ms of back-to-back steps have run,
+    # whatever --warmup asked for.
+    settle_steps, t_settle = 0, time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for i in range(64):
+            step(i % R)
+        settle_steps += 64
+        torch.cuda.synchronize()
+    log(f"[bench] settle {settle_steps} steps")
 
     K = args.steps
     # pass 1 (the figure): K back-to-back steps bracketed by two events only;
@@ -429,6 +458,18 @@ def main():
         step(i % R, evs[i])
     torch.cuda.synchronize()
     dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    # the cache-write kernel alone (one new token per sequence), back to back
+    n_w = 200
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
+    for i in range(n_w):
+        if fp8:
+            _lib.kv_cache_write_fp8(kps[i % R], vps[i % R], kn, vn, ksd, vsd, slots, stream=stream)
+        else:
+            _lib.kv_cache_write(kps[i % R], vps[i % R], kn, vn, slots, stream=stream)
+    w1.record(stream)
+    torch.cuda.synchronize()
+    write_us = w0.elapsed_time(w1) * 1e3 / n_w
 
     # compulsory bytes: K/V of each distinct cached token slot once (blocks that
     # several tables share, as in the shared-prompt workload, count once), Q, O
@@ -451,6 +492,7 @@ def main():
     achieved = call_bytes / (call_ms * 1e-3) / 1e9
     ptok, nparts = _lib.decode_plan(w.n_heads, w.n_kv_heads, w.block_size, w.num_seqs,
                                     w.max_blocks_per_seq)
+    traffic, traffic_source = measured_traffic(args.config, fused, fp8)
 
     result = {
         "metric": METRIC,
@@ -487,7 +529,7 @@ def main():
         "logical_kv_bytes": int(logical_kv),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(args.config, fused, fp8),
+                     "traffic": traffic, "traffic_source": traffic_source,
                      "kernel": ("paged_attn_decode_append" if fused else "paged_attn_decode") + ("_fp8" if fp8 else "")
                                + " call (decode kernel"
                                + (")" if nparts == 1 else
@@ -495,11 +537,13 @@ def main():
                                   " + partition merge kernel)"),
                      "algorithmic_bytes": int(call_bytes), "call_us": round(call_ms * 1e3, 3)},
         "wall_ms_per_step": round(wall * 1e3 / K, 5),
+        "settle_steps": settle_steps,
+        "write_kernel_us": {"us": round(write_us, 3), "tokens": n_written,
+                            "note": f"kv_cache_write{'_fp8' if fp8 else ''} alone, {n_w} calls back to back"},
     }
     if not args.no_ceiling:
-        log("[bench] stream ceiling")
-        rd, cp = stream_ceiling(dev)
-        result["stream_ceiling_gbs"] = {"torch_sum_read": round(rd, 1), "torch_copy_rw": round(cp, 1)}
+        log("[bench] read ceilings (probe kernels)")
+        result["stream_ceiling_gbs"] = stream_ceiling(dev)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         torch.cuda.synchronize()

@@ -54,10 +54,13 @@
  * race, as for pkv_paged_attn_decode.
  * Device-side checks: a sequence whose prefix_lens value is negative, not a
  * multiple of block_size or larger than seq_lens[s], or whose length exceeds
- * the table, gets NaN rows. A group range outside the batch, or prefix
- * lengths that differ within a group, break the precondition: results of
- * those sequences are undefined, and no memory outside the arguments and the
- * workspace is accessed.
+ * the table, gets NaN rows. Group ranges that do not cut the batch into
+ * consecutive groups, or prefix lengths that differ within a group, break the
+ * precondition. The one-launch path checks the whole description in the
+ * kernel and then writes NaN to every output row; the two-launch path leaves
+ * the results of the offending sequences undefined. Either way no memory
+ * outside the arguments and the workspace is accessed, and later calls on the
+ * stream are unaffected.
  */
 #ifndef PKV_SHARED_PREFIX_H
 #define PKV_SHARED_PREFIX_H

@@ -65,6 +65,9 @@ _SIGNATURES = {
                                                                _i32, _i64, _i32, _vp]),
     "pkv_paged_attn_chunk_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32,
                                                 _i32, _i32, _i32, _i32, _i64, _i32, _i32, _vp]),
+    # read-bandwidth probes (pkv_probe.h)
+    "pkv_probe_stream_read": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp]),
+    "pkv_probe_gather_tiles": (ctypes.c_int, [_vp, _i64, _vp, _i64, _i32, _i32, _vp, _vp]),
     # FP8 (e4m3) KV cache (pkv_fp8.h)
     "pkv_paged_attn_decode_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32,
                                                  _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
@@ -135,6 +138,12 @@ def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
     ``block_tables`` int32 ``[B, MB]``; ``seq_lens`` int32 ``[B]``.
     Enqueued on ``stream`` (default: the current stream of ``q``'s device).
     """
+    return _decode("pkv_paged_attn_decode", out, q, k_pool, v_pool, block_tables, seq_lens, scale, n_heads,
+                   n_kv_heads, head_dim, block_size, stream)
+
+
+def _decode(symbol, out, q, k_pool, v_pool, block_tables, seq_lens, scale, n_heads, n_kv_heads, head_dim,
+            block_size, stream):
     dt = q.dtype
     _need(dt in DTYPE_CODES, f"unsupported dtype {dt}")
     for name, t in (("out", out), ("q", q), ("k_pool", k_pool), ("v_pool", v_pool)):
@@ -151,7 +160,7 @@ def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
     devs = {t.device for t in (out, q, k_pool, v_pool, block_tables, seq_lens)}
     _need(len(devs) == 1, "all tensors must be on one device")
     with torch.cuda.device(q.device):
-        _check(lib().pkv_paged_attn_decode(
+        _check(getattr(lib(), symbol)(
             out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
             block_tables.data_ptr(), seq_lens.data_ptr(), float(scale), n_heads, n_kv_heads,
             head_dim, block_size, B, block_tables.shape[1], k_pool.shape[0], DTYPE_CODES[dt],
@@ -388,6 +397,7 @@ def paged_attn_chunk(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v
         _dev_tensor(t, name, dt)
     for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens), ("query_start_loc", query_start_loc)):
         _dev_tensor(t, name, torch.int32)
+    _need(seq_lens.dim() == 1, "seq_lens must be [B]")
     B = seq_lens.shape[0]
     _need(q.dim() == 3 and q.shape[1:] == (n_heads, head_dim) and out.shape == q.shape, "q/out must be [T, H, D]")
     _need(k_pool.dim() == 4 and k_pool.shape[1:] == (n_kv_heads, block_size, head_dim),
@@ -421,6 +431,7 @@ def paged_attn_decode_shared_prefix(out: torch.Tensor, q: torch.Tensor, k_pool: 
     for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens), ("prefix_lens", prefix_lens),
                     ("group_start", group_start)):
         _dev_tensor(t, name, torch.int32)
+    _need(seq_lens.dim() == 1, "seq_lens must be [B]")
     B = seq_lens.shape[0]
     _need(q.shape == (B, n_heads, head_dim) and out.shape == q.shape, "q/out must be [B, H, D]")
     _need(k_pool.dim() == 4 and k_pool.shape[1:] == (n_kv_heads, block_size, head_dim),
@@ -480,6 +491,7 @@ def paged_attn_chunk_fp8(out, q, k_pool, v_pool, k_scale, v_scale, block_tables,
     _fp8_pools(k_pool, v_pool, k_scale, v_scale, n_kv_heads, block_size, head_dim)
     for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens), ("query_start_loc", query_start_loc)):
         _dev_tensor(t, name, torch.int32)
+    _need(seq_lens.dim() == 1, "seq_lens must be [B]")
     B = seq_lens.shape[0]
     _need(q.dim() == 3 and q.shape[1:] == (n_heads, head_dim) and out.shape == q.shape, "q/out must be [T, H, D]")
     _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B, MB]")
@@ -505,6 +517,7 @@ def paged_attn_decode_shared_prefix_fp8(out, q, k_pool, v_pool, k_scale, v_scale
     for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens), ("prefix_lens", prefix_lens),
                     ("group_start", group_start)):
         _dev_tensor(t, name, torch.int32)
+    _need(seq_lens.dim() == 1, "seq_lens must be [B]")
     B = seq_lens.shape[0]
     _need(q.shape == (B, n_heads, head_dim) and out.shape == q.shape, "q/out must be [B, H, D]")
     _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B, MB]")
@@ -532,6 +545,7 @@ def paged_attn_decode_append(out, q, k_pool, v_pool, k_new, v_new, block_tables,
         _dev_tensor(t, name, dt)
     for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens)):
         _dev_tensor(t, name, torch.int32)
+    _need(seq_lens.dim() == 1, "seq_lens must be [B]")
     B = seq_lens.shape[0]
     _need(q.shape == (B, n_heads, head_dim) and out.shape == q.shape, "q/out must be [B, H, D]")
     _need(k_new.shape == (B, n_kv_heads, head_dim) and v_new.shape == k_new.shape, "k_new/v_new must be [B, Hkv, D]")
@@ -539,6 +553,8 @@ def paged_attn_decode_append(out, q, k_pool, v_pool, k_new, v_new, block_tables,
           "k_pool must be [NB, Hkv, BS, D]")
     _need(v_pool.shape == k_pool.shape, "v_pool must match k_pool")
     _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B, MB]")
+    devs = {t.device for t in (out, q, k_pool, v_pool, k_new, v_new, block_tables, seq_lens)}
+    _need(len(devs) == 1, "all tensors must be on one device")
     with torch.cuda.device(q.device):
         _check(lib().pkv_paged_attn_decode_append(
             out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
@@ -565,6 +581,7 @@ def paged_attn_decode_append_fp8(out, q, k_pool, v_pool, k_new, v_new, k_scale, 
         _need(t.shape == (n_kv_heads,), f"{name} must be [Hkv]")
     for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens)):
         _dev_tensor(t, name, torch.int32)
+    _need(seq_lens.dim() == 1, "seq_lens must be [B]")
     B = seq_lens.shape[0]
     _need(q.shape == (B, n_heads, head_dim) and out.shape == q.shape, "q/out must be [B, H, D]")
     _need(k_new.shape == (B, n_kv_heads, head_dim) and v_new.shape == k_new.shape, "k_new/v_new must be [B, Hkv, D]")
@@ -581,3 +598,29 @@ def paged_attn_decode_append_fp8(out, q, k_pool, v_pool, k_new, v_new, k_scale, 
             n_heads, n_kv_heads, head_dim, block_size, B, block_tables.shape[1], k_pool.shape[0], DTYPE_CODES[dt],
             _stream_handle(q, stream)))
     return out
+
+
+def probe_stream_read(buf: torch.Tensor, grid: int, sink: torch.Tensor, stream=None) -> None:
+    """Read every 16-byte unit of ``buf`` once (``pkv_probe_stream_read``);
+    ``sink`` is a uint32/int32 device tensor of at least ``grid`` entries."""
+    _dev_tensor(buf, "buf")
+    _dev_tensor(sink, "sink")
+    _need(sink.element_size() == 4 and sink.numel() >= grid, "sink must hold grid 32-bit words")
+    with torch.cuda.device(buf.device):
+        _check(lib().pkv_probe_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), int(grid),
+                                           sink.data_ptr(), _stream_handle(buf, stream)))
+
+
+def probe_gather_tiles(pool: torch.Tensor, tiles: torch.Tensor, depth: int, grid: int, sink: torch.Tensor,
+                       stream=None) -> None:
+    """Read the 4096-byte tiles of ``pool`` listed in ``tiles`` (int32), the
+    decode kernel's gather pattern (``pkv_probe_gather_tiles``)."""
+    _dev_tensor(pool, "pool")
+    _dev_tensor(tiles, "tiles", torch.int32)
+    _dev_tensor(sink, "sink")
+    nbytes = pool.numel() * pool.element_size()
+    _need(nbytes % 4096 == 0, "pool must be whole 4096-byte tiles")
+    _need(sink.element_size() == 4 and sink.numel() >= grid, "sink must hold grid 32-bit words")
+    with torch.cuda.device(pool.device):
+        _check(lib().pkv_probe_gather_tiles(pool.data_ptr(), nbytes // 4096, tiles.data_ptr(), tiles.numel(),
+                                            int(depth), int(grid), sink.data_ptr(), _stream_handle(pool, stream)))

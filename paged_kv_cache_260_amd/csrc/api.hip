@@ -130,9 +130,14 @@ int get_workspace(hipStream_t stream, size_t bytes, void **out) {
   return PKV_OK;
 }
 
-// Arrival counters of the in-kernel partition merge, one set per (device,
-// stream): zeroed when allocated, and every call leaves them at zero again.
+// Counters of the decode-kernel family, one buffer per (device, stream),
+// zeroed when allocated: the late workgroups' ticket counter in the first
+// kTicketInts ints (any value works, tickets.h), then the arrival counters of
+// the in-kernel partition merge, which every call leaves at zero again (the
+// partitions of a row set agree on their count; shared-prefix calls whose
+// description is broken count nothing).
 std::map<std::pair<int, hipStream_t>, Workspace> g_arrivals;
+constexpr int64_t kTicketInts = 64;
 
 int get_arrivals(hipStream_t stream, int64_t count, int32_t **out) {
   int dev = 0;
@@ -269,21 +274,23 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
     return fail(PKV_ERR_INVALID, "%d sequences x %d partitions x %d heads: too many workgroups",
                 num_seqs, a.max_parts, n_kv_heads);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // counters, one buffer per (device, stream): the ticket counter of the
-  // late workgroups first, then (in-kernel merge) the arrival counters
-  constexpr int64_t kTicketInts = 64;
+  // counters: the ticket counter of the late workgroups first, then (in-kernel
+  // merge) the arrival counters; split partials: [acc rows x D | (m, l) rows]
   const bool fused_merge = a.max_parts > 1 && a.max_parts <= pkv::kFusedMergeParts;
+  const int64_t counter_ints = kTicketInts + (fused_merge ? (int64_t)num_seqs * n_kv_heads * a.head_chunks : 0);
+  const size_t rows = a.max_parts > 1 ? (size_t)num_seqs * n_heads * a.max_parts : 0;
+  const size_t acc_bytes = rows * head_dim * sizeof(float);
+  const size_t ws_bytes = acc_bytes + rows * sizeof(float2);
   int32_t *counters = nullptr;
-  int rc = get_arrivals(st, kTicketInts + (fused_merge ? (int64_t)num_seqs * n_kv_heads * a.head_chunks : 0),
-                        &counters);
+  void *ws = nullptr;
+  int rc = get_arrivals(st, counter_ints, &counters);
   if (rc != PKV_OK) return rc;
-  a.tickets = reinterpret_cast<uint32_t *>(counters);
-  if (a.max_parts > 1) {
-    const size_t rows = (size_t)num_seqs * n_heads * a.max_parts;
-    const size_t acc_bytes = rows * head_dim * sizeof(float);
-    void *ws = nullptr;
-    rc = get_workspace(st, acc_bytes + rows * sizeof(float2), &ws);
+  if (rows) {
+    rc = get_workspace(st, ws_bytes, &ws);
     if (rc != PKV_OK) return rc;
+  }
+  a.tickets = reinterpret_cast<uint32_t *>(counters);
+  if (rows) {
     a.part_acc = static_cast<float *>(ws);
     a.part_ml = reinterpret_cast<float2 *>(static_cast<char *>(ws) + acc_bytes);
     if (fused_merge) a.arrivals = counters + kTicketInts;
@@ -405,7 +412,6 @@ int chunk_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
     if (items * a.max_parts > (int64_t)INT32_MAX) return fail(PKV_ERR_INVALID, "too many work items");
     // the late workgroups' ticket counter first, then the arrival counters
     // (as in decode)
-    constexpr int64_t kTicketInts = 64;
     const bool fused_merge = a.max_parts > 1 && a.max_parts <= pkv::kFusedMergeParts;
     int32_t *counters = nullptr;
     int rc = get_arrivals(st, kTicketInts + (fused_merge ? items : 0), &counters);
@@ -549,7 +555,13 @@ int shared_prefix_impl(void *out, const void *q, const void *k_pool, const void 
   // One launch for both kinds of work item when every group's rows fit one
   // 16-row block per KV head and the partial slots per (sequence, head) fit
   // the in-kernel merge.
-  if (group <= 16 && (group & (group - 1)) == 0 && (int64_t)max_group_size * group <= 16) {
+  // The kernel's longest-first plan checks the sharing description (a broken
+  // one must not unbalance the arrival counts), so the one-launch path is
+  // taken only for batches that plan covers.
+  pkv::DecodeArgs ent = suf;
+  ent.num_seqs = num_groups + num_seqs;
+  if (group <= 16 && (group & (group - 1)) == 0 && (int64_t)max_group_size * group <= 16 &&
+      num_groups + num_seqs <= 65535 && pkv::decode_compact_plan(ent)) {
     int64_t p_pre = suf.partition_tokens, n_pre = suf.max_parts;
     if (g_partition_override.load() <= 0) {
       // shortest prefix partition whose count fits the slots the private
@@ -580,8 +592,10 @@ int shared_prefix_impl(void *out, const void *q, const void *k_pool, const void 
       if (rc != PKV_OK) return rc;
       a.part_acc = static_cast<float *>(ws);
       a.part_ml = reinterpret_cast<float2 *>(static_cast<char *>(ws) + acc_bytes);
-      rc = get_arrivals(st, (int64_t)num_seqs * n_kv_heads, &a.arrivals);
+      int32_t *counters = nullptr;
+      rc = get_arrivals(st, kTicketInts + (int64_t)num_seqs * n_kv_heads, &counters);
       if (rc != PKV_OK) return rc;
+      a.arrivals = counters + kTicketInts;
       hipError_t e = pkv::launch_shared_fused(static_cast<pkv::DType>(dtype), head_dim, fp8, a, st);
       if (e != hipSuccess) return hip_fail(e, "shared-prefix decode launch");
       return ok();
@@ -635,10 +649,11 @@ int shared_prefix_impl(void *out, const void *q, const void *k_pool, const void 
   if (pre_fused || suf_fused) {
     // one counter set serves both launches: each leaves its counters at zero
     int32_t *arr = nullptr;
-    rc = get_arrivals(st, std::max(pre_fused ? pre_items : 0, suf_fused ? (int64_t)num_seqs * suf_units : 0), &arr);
+    rc = get_arrivals(st, kTicketInts + std::max(pre_fused ? pre_items : 0, suf_fused ? (int64_t)num_seqs * suf_units : 0),
+                      &arr);
     if (rc != PKV_OK) return rc;
-    if (pre_fused) pre.arrivals = arr;
-    if (suf_fused) suf.arrivals = arr;
+    if (pre_fused) pre.arrivals = arr + kTicketInts;
+    if (suf_fused) suf.arrivals = arr + kTicketInts;
   }
   hipError_t e = pkv::launch_shared_prefix(static_cast<pkv::DType>(dtype), head_dim, fp8, pre, suf, st);
   if (e != hipSuccess) return hip_fail(e, "shared-prefix decode launch");

@@ -39,6 +39,7 @@
 #include "attn_common.h"
 #include "fp8_encode.h"
 #include "kernels.h"
+#include "tickets.h"
 
 #include <math.h>
 
@@ -162,7 +163,12 @@ struct ItemPlan {
   int full_items;  // full partitions of the batch (uniform)
   int items;       // all items of one unit (uniform)
   int p_pre;       // shared mode: partition length of the prefix entities (uniform)
+  bool bad_desc;   // shared mode: the sharing description breaks its precondition (uniform)
 };
+
+// Shared mode: a prefix item's rows are at most this many (member, head)
+// pairs, so a group has at most kSharedRows / group members.
+constexpr int kSharedRows = 16;
 
 
 // Inclusive prefix sum over the wave with DPP (no LDS round trips): shifts
@@ -212,22 +218,46 @@ __device__ __forceinline__ void make_plan(const DecodeArgs &a, ItemPlan &pl, int
   int L;       // tokens the entity's items walk
   int Pe = P;  // its partition length
   pl.p_pre = a.prefix_partition_tokens;
+  pl.bad_desc = false;
   if constexpr (MODE == kModeShared) {
     // entities: the groups' prefixes, then the sequences' private tokens
     const int ng = a.num_groups;
     const bool is_pre = e < ng;
     const int first = ec < ng ? a.query_start_loc[ec] : ec - ng;
+    const int gend = ec < ng ? a.query_start_loc[ec + 1] : first + 1;
     const int m = min(max(first, 0), a.member_seqs - 1);
     const int len = a.seq_lens[m];
     const int pre = a.prefix_lens[m];
+    // The arrival counts of the prefix and private partitions of a sequence
+    // agree only if the description holds: the groups cut [0, member_seqs)
+    // into consecutive ranges of at most kSharedRows / group members, and a
+    // group's members share one prefix length. Each group lane checks its own
+    // range and members; one violation anywhere makes the whole call write
+    // NaN rows and count no arrivals, so the counters stay at zero.
+    bool bad = false;
+    if (in && is_pre) {
+      const int nmem = gend - first;
+      bad = first < 0 || nmem < 1 || gend > a.member_seqs || nmem * a.group > kSharedRows ||
+            (e == 0 && first != 0) || (e == ng - 1 && gend != a.member_seqs);
+      int mp[kSharedRows - 1];
+#pragma unroll
+      for (int k = 0; k < kSharedRows - 1; ++k) mp[k] = a.prefix_lens[min(m + 1 + k, a.member_seqs - 1)];
+#pragma unroll
+      for (int k = 0; k < kSharedRows - 1; ++k) bad |= k + 1 < nmem && mp[k] != pre;
+    }
     L = is_pre ? pre : (pre >= 0 && pre <= len ? len - pre : -1);
     int max_private = !is_pre && in && (int64_t)len <= max_tok ? max(L, 0) : 0;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) max_private = max(max_private, __shfl_xor(max_private, d, 64));
-    if (lane == 0) sp[kPlanAux + c] = max_private;
+    const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0ull;  // every lane votes (outside the branch)
+    if (lane == 0) sp[kPlanAux + c] = wave_bad ? -1 : max_private;
     __syncthreads();
 #pragma unroll
-    for (int cc = 0; cc < kCompactChunks; ++cc) max_private = max(max_private, sp[kPlanAux + cc]);
+    for (int cc = 0; cc < kCompactChunks; ++cc) {
+      const int v = sp[kPlanAux + cc];
+      pl.bad_desc |= v < 0;
+      max_private = max(max_private, v);
+    }
     pl.p_pre = __builtin_amdgcn_readfirstlane(shared_prefix_partition(a, max_private));
     Pe = is_pre ? pl.p_pre : P;
   } else if constexpr (MODE == kModePrefix) {
@@ -393,8 +423,8 @@ __device__ __forceinline__ void load_item_head(const DecodeArgs &a, int tid, int
 
 template <typename T, int D, int GT, bool F8, int MODE>
 __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int tid, int unit, int s, int part,
-                                            int p_pre, ItemHead<Cfg<T, D, GT>::kQPer> &hd, int s_next,
-                                            int part_next) {
+                                            int p_pre, bool bad_desc, ItemHead<Cfg<T, D, GT>::kQPer> &hd,
+                                            int s_next, int part_next) {
   using C = Cfg<T, D, GT>;
   // rows mode: item rows are (token or member, head) pairs
   constexpr bool RM = MODE == kModeChunk || MODE == kModePrefix || MODE == kModeShared;
@@ -437,6 +467,15 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
       nq = 1;
     }
     bad_rows = q0 < 0 || nq < 1 || q0 + nq > a.member_seqs;
+    if (bad_desc) {
+      // the sharing description is broken (make_plan): each sequence's first
+      // private item writes its NaN rows, nothing else runs or counts
+      if (!pre_item && part == 0 && !bad_rows) {
+        for (int i = tid; i < min(GT, G) * D; i += kNW * 64)
+          out[((int64_t)q0 * H + g * G + i / D) * D + i % D] = static_cast<T>(__builtin_nanf(""));
+      }
+      return;
+    }
   } else if constexpr (RM) {
     q0 = a.query_start_loc[s];
     nq = a.query_start_loc[s + 1] - q0;
@@ -1098,6 +1137,22 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   // agent-scope loads (never stale lines of its XCD's L2), resets the counter
   // for the next call and writes the merged rows:
   //   M = max_p m_p,  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+  //
+  // Ordering. No fence is used; the argument rests on how gfx950 executes
+  // these accesses, not on the language memory model (where relaxed atomics
+  // alone would not order the partial stores before the increment):
+  //   - agent-scope atomic stores and loads bypass the XCD-local L2 for
+  //     coherence (stores write through, loads miss to memory), so a store
+  //     that has completed is visible to an agent-scope load from any XCD;
+  //   - a wave's vector-memory stores count in vmcnt until the memory side
+  //     acknowledges them, so "s_waitcnt vmcnt(0)" below returns only after
+  //     every partial store of this wave has completed, and the barrier after
+  //     it extends that to the workgroup before thread 0 increments;
+  //   - the last arriver's loads are issued only after its increment has
+  //     returned (they depend on its value through the flag in LDS).
+  // The release/acquire pair the compiler would emit adds a writeback and an
+  // invalidate of the whole L2 around plain stores, which this data does not
+  // need; it measured 3-10x slower.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   int *flag = reinterpret_cast<int *>(smem + C::kFlagOff);
@@ -1215,20 +1270,21 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT, F8>()))) void p
   const int units = a.n_kv_heads * a.head_chunks;
   const bool compact = compact_plan(a);
   // A workgroup past the first static_wgs takes the place of workgroup
-  // static_wgs + ticket: the claimers together cover exactly those places,
-  // in the order their slots free up on any XCD (the counter wraps to zero
-  // after the last of the gridDim - static_wgs tickets). The fixed map sends
-  // workgroup i to XCD i mod 8, and XCDs finish their equal shares several
-  // microseconds apart; tickets let the later, shorter items go to the XCDs
-  // that are ahead.
+  // static_wgs + ticket_place(ticket): the claimers together cover exactly
+  // those places, in the order their slots free up on any XCD, whatever value
+  // the counter starts from (tickets.h; a clean call leaves it where it
+  // started). The fixed map sends workgroup i to XCD i mod 8, and XCDs finish
+  // their equal shares several microseconds apart; tickets let the later,
+  // shorter items go to the XCDs that are ahead.
   const bool claim = compact && a.tickets != nullptr && (int64_t)blockIdx.x >= a.static_wgs;
+  const uint32_t claimers = gridDim.x - (uint32_t)a.static_wgs;  // >= 1 whenever tickets are on
   uint32_t ticket = 0;
   if (claim && threadIdx.x == 0)
-    ticket = __builtin_amdgcn_atomic_inc32(a.tickets, gridDim.x - (uint32_t)a.static_wgs - 1u, __ATOMIC_RELAXED,
-                                           "agent");
+    ticket = __builtin_amdgcn_atomic_inc32(a.tickets, claimers - 1u, __ATOMIC_RELAXED, "agent");
   ItemPlan plan;
   plan.p_pre = a.prefix_partition_tokens;
   plan.full_items = plan.items = 0;
+  plan.bad_desc = false;
   int *plan_lds = reinterpret_cast<int *>(smem + Cfg<T, D, GT>::kPlanOff);
   if (compact) make_plan<MODE>(a, plan, plan_lds, claim, ticket);
   // Tickets place items only when every workgroup takes one item (a unit has
@@ -1236,16 +1292,16 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT, F8>()))) void p
   // fixed places measured faster. Every claimer has drawn its ticket either
   // way, so the counter still wraps to zero.
   const bool placed = claim && plan.items <= a.wgs_per_unit;
-  const int64_t lin = placed ? (int64_t)a.static_wgs + __builtin_amdgcn_readfirstlane(plan_lds[kPlanTicket])
-                             : (int64_t)blockIdx.x;
+  const int64_t lin =
+      placed ? (int64_t)a.static_wgs +
+                   ticket_place((uint32_t)__builtin_amdgcn_readfirstlane(plan_lds[kPlanTicket]), claimers)
+             : (int64_t)blockIdx.x;
   const int unit = (int)(lin % units);
   const int w = (int)(lin / units);
   ItemHead<Cfg<T, D, GT>::kQPer> hd{};
   hd.ready = false;
   // item j of this workgroup's walk (compact plans), or -1 past its end
-  const bool lin_ok = lin < (int64_t)gridDim.x;  // a ticket past the call's range (never, with a clean counter)
   auto item_of = [&](int round) -> int64_t {
-    if (!lin_ok) return -1;
     const int G = a.wgs_per_unit;
     const int64_t j = (int64_t)round * G + ((round & 1) ? G - 1 - w : w);
     return j < plan.items ? j : -1;
@@ -1277,8 +1333,10 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT, F8>()))) void p
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     // prefix partition length (shared mode): the plan's, or the host's minimum
+    // shared mode: a description is checked only by the longest-first plan,
+    // which the host always picks for one-launch shared calls
     decode_item<T, D, GT, F8, MODE>(a, smem, tid, unit, s, part, compact ? plan.p_pre : a.prefix_partition_tokens,
-                                    hd, s_next, part_next);
+                                    !compact || plan.bad_desc, hd, s_next, part_next);
     s = s_next;
     part = part_next;
   }
@@ -1633,6 +1691,8 @@ hipError_t launch_zero_i32(int32_t *p, int64_t n, hipStream_t stream) {
                      stream, p, n);
   return hipGetLastError();
 }
+
+bool decode_compact_plan(const DecodeArgs &a) { return compact_plan(a); }
 
 int decode_head_tile(int group) {
   int gt = 1;

@@ -97,6 +97,10 @@ int decode_head_tile(int group);
 
 hipError_t launch_decode(DType dt, int head_dim, const DecodeArgs &a, hipStream_t stream);
 
+// True when a launch with these arguments takes the longest-first item order
+// that every workgroup builds from the lengths (a.num_seqs counts entities).
+bool decode_compact_plan(const DecodeArgs &a);
+
 // Multi-token (chunk) attention: the last n_s tokens of each sequence, causal.
 struct ChunkArgs {
   void *out;                       // [T, n_heads, head_dim]

@@ -46,7 +46,9 @@ class OnGpu:
 
 
 def oracle_decode(w, seq_lens, k_pool, v_pool, kv_heads=None, q=None) -> np.ndarray:
-    """Oracle output ``[B, H, D]`` (NaN where a KV head is not sampled), one KV head at a time."""
+    """Oracle output ``[B, H, D]``, one KV head at a time; with ``kv_heads``
+    only those heads' query rows are computed (the others hold NaN, and a
+    comparison must then name the rows it covers, see ``max_abs_err``)."""
     q = w.q if q is None else q
     G = w.group
     B, H, D = q.shape
@@ -71,8 +73,18 @@ def oracle_write(w, k_pool, v_pool):
     return torch.from_numpy(kp).view(w.dtype), torch.from_numpy(vp).view(w.dtype)
 
 
-def max_abs_err(gpu_out: torch.Tensor, ref: np.ndarray) -> float:
+def max_abs_err(gpu_out: torch.Tensor, ref: np.ndarray, rows=None) -> float:
+    """Largest |gpu - ref| over the compared elements: all of them, or those
+    ``rows`` selects (a boolean mask or index over the leading dimensions).
+    The reference must be finite wherever it is compared (a NaN there is an
+    oracle or fixture fault, never a reason to compare less), and so must the
+    GPU output."""
     got = gpu_out.detach().to("cpu", torch.float64).numpy()
-    mask = ~np.isnan(ref)
-    assert np.all(np.isfinite(got[mask])), "non-finite output"
-    return float(np.max(np.abs(got[mask] - ref[mask]))) if mask.any() else 0.0
+    ref = np.asarray(ref)
+    assert got.shape == ref.shape, f"shape {got.shape} vs reference {ref.shape}"
+    if rows is not None:
+        got, ref = got[rows], ref[rows]
+    assert ref.size > 0, "nothing compared"
+    assert np.all(np.isfinite(ref)), "non-finite reference among the compared elements"
+    assert np.all(np.isfinite(got)), "non-finite output"
+    return float(np.max(np.abs(got - ref)))

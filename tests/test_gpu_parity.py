@@ -53,19 +53,40 @@ def test_config_decode_parity(cfg):
     assert err <= TOL[w.dtype]
 
 
-def test_config4_long_context_sampled():
-    """Full-size long-context batch; the oracle checks two KV heads of every sequence."""
-    say("decode parity cfg4 (sampled kv heads 0 and 7)")
-    w = workloads.make(4)
+@pytest.fixture(scope="module")
+def config4():
+    """The full-size long-context batch (4 sequences of 32K, 64K, 96K and 128K
+    tokens, GQA 32/8, NaN in every slot no sequence may read) and the oracle's
+    output for every query head of every sequence (computed once, one KV head
+    at a time)."""
+    say("cfg4: building the workload and the oracle reference (all 8 KV heads)")
+    w = workloads.make(4, poison=True)
+    ref = oracle_decode(w, w.seq_lens, w.k_pool, w.v_pool)
+    assert np.isfinite(ref).all()
+    return w, ref
+
+
+@pytest.mark.parametrize("partition,expect_parts", [(0, 129), (512, 257)])
+def test_config4_long_context_all_heads(config4, partition, expect_parts):
+    """Every output row of the long-context batch against the oracle: at the
+    library's automatic 1024-token partitions (32-128 per sequence) and at the
+    configuration's 512-token partitions (64-256 per sequence, 640 partials
+    per query head). Both exceed the in-kernel merge, so the cross-partition
+    merge kernel combines them. (The tables hold one block more than the
+    longest sequence needs, room for its next token, hence one more partition
+    in the plan's maximum.)"""
+    w, ref = config4
+    _lib.set_partition_tokens(partition)
+    ptok, nparts = _lib.decode_plan(w.n_heads, w.n_kv_heads, 16, 4, w.max_blocks_per_seq)
+    say(f"decode parity cfg4, partition {ptok} tokens, up to {nparts} partitions, all KV heads")
+    assert (ptok, nparts) == (partition or 1024, expect_parts)
     g = OnGpu(w)
-    assert _lib.decode_plan(w.n_heads, w.n_kv_heads, 16, 4, w.max_blocks_per_seq)[0] == 1024
-    out = g.decode()
+    out = torch.full_like(g.q, float("nan"))
+    g.decode(out=out)
     torch.cuda.synchronize()
-    ref = oracle_decode(w, w.seq_lens, w.k_pool, w.v_pool, kv_heads=[0, 7])
     err = max_abs_err(out, ref)
-    say(f"cfg4 max abs err {err:.3e}")
+    say(f"cfg4 partition {ptok}: max abs err {err:.3e} over {ref.size} outputs")
     assert err <= TOL[w.dtype]
-    assert torch.isfinite(out).all()
 
 
 @pytest.mark.parametrize("cfg", [1, 3, 5])

@@ -45,17 +45,18 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_gpu(w, group_start, prefix_lens, seq_lens=None):
+def run_gpu(w, group_start, prefix_lens, seq_lens=None, max_group_size=None, fill=float("nan")):
     dev = "cuda"
     lens = w.seq_lens if seq_lens is None else seq_lens
     q = w.q.to(dev)
-    out = torch.empty_like(q)
+    out = torch.full_like(q, fill)  # a row the call skips keeps the fill
     gs = np.asarray(group_start, dtype=np.int32)
+    mg = int(np.diff(gs).max()) if max_group_size is None else max_group_size
     _lib.paged_attn_decode_shared_prefix(
         out, q, w.k_pool.to(dev), w.v_pool.to(dev), torch.from_numpy(w.block_tables).to(dev),
         torch.from_numpy(np.asarray(lens, np.int32)).to(dev),
         torch.from_numpy(np.asarray(prefix_lens, np.int32)).to(dev), torch.from_numpy(gs).to(dev), w.scale,
-        w.n_heads, w.n_kv_heads, w.head_dim, w.block_size, int(np.diff(gs).max()))
+        w.n_heads, w.n_kv_heads, w.head_dim, w.block_size, mg)
     torch.cuda.synchronize()
     return out
 
@@ -177,10 +178,52 @@ def test_single_launch_groups(H, Hkv, D, BS, dtype, sizes, pblk, partition):
 
 
 def test_single_launch_many_entities():
-    """100 groups of 4 samples (500 work entities: past the longest-first
-    planner's limit) in one launch."""
+    """100 groups of 4 samples: 500 work entities, past the longest-first
+    plan's limit. The one-launch path needs that plan (it checks the sharing
+    description), so these shapes take the two launches."""
     rng = np.random.default_rng(12)
     w, gs, pl = groups_case(12, [4] * 100, [int(x) for x in rng.integers(0, 20, 100)], 16, 4, 64, 16,
                             torch.float16, max_private=300)
     out = run_gpu(w, gs, pl)
     assert max_abs_err(out, run_oracle(w)) <= TOL[w.dtype]
+
+
+def plain_decode_gpu(w):
+    dev = "cuda"
+    out = torch.full(tuple(w.q.shape), float("nan"), dtype=w.dtype, device=dev)
+    _lib.paged_attn_decode(out, w.q.to(dev), w.k_pool.to(dev), w.v_pool.to(dev),
+                           torch.from_numpy(w.block_tables).to(dev), torch.from_numpy(w.seq_lens).to(dev), w.scale,
+                           w.n_heads, w.n_kv_heads, w.head_dim, w.block_size)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("broken", ["prefix_mismatch", "range_gap", "range_disorder"])
+def test_broken_description_is_nan_and_leaves_later_calls_intact(broken):
+    """A one-launch call whose description breaks the precondition (a member
+    claims a shorter prefix than its group; the last sequence belongs to no
+    group; a group boundary lies before the previous one) writes NaN to every
+    output row and counts no arrivals. Then, on the same stream, a
+    128-sequence plain decode (whose late workgroups draw tickets, and whose
+    partitions use the same counters) and a valid shared-prefix call of the
+    first batch both match the oracle."""
+    say(f"broken description: {broken}")
+    w, gs, pl = groups_case(13, [4, 4, 2, 4], [10, 3, 0, 6], 32, 8, 128, 16, torch.bfloat16, max_private=900)
+    gs_bad, pl_bad = gs.copy(), pl.copy()
+    if broken == "prefix_mismatch":
+        pl_bad[1] -= 2 * w.block_size
+    elif broken == "range_gap":
+        gs_bad[-1] -= 1
+    else:
+        gs_bad[2] = gs[1] - 1
+    # the host sees groups of at most 4 members (4 x 4 rows): one launch
+    out = run_gpu(w, gs_bad, pl_bad, max_group_size=4, fill=0.0)
+    assert torch.isnan(out.float()).all()
+    big = workloads.random_case(91, num_seqs=128, n_heads=32, n_kv_heads=8, head_dim=128, block_size=16,
+                                dtype=torch.bfloat16, max_len=3000, min_len=16, poison=True)
+    err = max_abs_err(plain_decode_gpu(big), run_oracle(big))
+    say(f"  plain decode after it: max abs err {err:.3e}")
+    assert err <= TOL[big.dtype]
+    err = max_abs_err(run_gpu(w, gs, pl), run_oracle(w))
+    say(f"  valid shared call after it: max abs err {err:.3e}")
+    assert err <= TOL[w.dtype]
