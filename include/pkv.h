@@ -172,6 +172,34 @@ PKV_API int pkv_paged_attn_decode_append(void *out, const void *q, void *k_pool,
                                          int32_t block_size, int32_t num_seqs, int32_t max_blocks_per_seq,
                                          int64_t num_blocks, int32_t dtype, void *stream);
 
+/*
+ * pkv_paged_attn_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments, result, checks and kernels as
+ * pkv_paged_attn_decode (outputs are bit-identical); the only difference is
+ * where the kernels keep their scratch (the split partials and the merge
+ * counters): a fixed array compiled into the library, one per GPU, held until
+ * the process ends, instead of a workspace grown on demand. The call makes no
+ * allocation: the first call on a device looks up that device's array and
+ * clears its counters with a small kernel on `stream`.
+ *
+ * Limits (PKV_ERR_INVALID beyond them, before anything is launched):
+ *   split partials  num_seqs * n_heads * P * (head_dim + 2) * 4 bytes
+ *                   <= PKV_NOALLOC_WORKSPACE_BYTES, with P the partition count
+ *                   pkv_decode_plan reports (no partials when P = 1);
+ *   merge counters  num_seqs * n_kv_heads * ceil(n_heads / n_kv_heads / 16)
+ *                   + 64 <= PKV_NOALLOC_COUNTERS when 1 < P <= 8.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (different streams or host threads) race and must not be issued.
+ */
+#define PKV_NOALLOC_WORKSPACE_BYTES (64u << 20)
+#define PKV_NOALLOC_COUNTERS 16384
+PKV_API int pkv_paged_attn_decode_noalloc(void *out, const void *q, const void *k_pool, const void *v_pool,
+                                          const int32_t *block_tables, const int32_t *seq_lens, float scale,
+                                          int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                                          int32_t block_size, int32_t num_seqs, int32_t max_blocks_per_seq,
+                                          int64_t num_blocks, int32_t dtype, void *stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 PKV_API const char *pkv_last_error(void);
 

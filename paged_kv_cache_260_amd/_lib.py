@@ -29,6 +29,8 @@ _i32, _i64, _f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c
 _SIGNATURES = {
     "pkv_paged_attn_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32, _i32,
                                              _i32, _i32, _i32, _i64, _i32, _vp]),
+    "pkv_paged_attn_decode_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32, _i32,
+                                                     _i32, _i32, _i32, _i64, _i32, _vp]),
     "pkv_kv_cache_write": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64,
                                           _i32, _vp]),
     "pkv_last_error": (ctypes.c_char_p, []),
@@ -140,6 +142,17 @@ def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
     """
     return _decode("pkv_paged_attn_decode", out, q, k_pool, v_pool, block_tables, seq_lens, scale, n_heads,
                    n_kv_heads, head_dim, block_size, stream)
+
+
+def paged_attn_decode_noalloc(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
+                              v_pool: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                              scale: float, n_heads: int, n_kv_heads: int, head_dim: int,
+                              block_size: int, stream=None) -> torch.Tensor:
+    """``paged_attn_decode`` with its scratch in the library's fixed per-GPU
+    array instead of an allocated workspace (``pkv_paged_attn_decode_noalloc``:
+    the call allocates nothing; sizes past the array's limits raise)."""
+    return _decode("pkv_paged_attn_decode_noalloc", out, q, k_pool, v_pool, block_tables, seq_lens, scale,
+                   n_heads, n_kv_heads, head_dim, block_size, stream)
 
 
 def _decode(symbol, out, q, k_pool, v_pool, block_tables, seq_lens, scale, n_heads, n_kv_heads, head_dim,

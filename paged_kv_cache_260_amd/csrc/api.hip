@@ -168,6 +168,44 @@ int get_arrivals(hipStream_t stream, int64_t count, int32_t **out) {
   return PKV_OK;
 }
 
+// Scratch of pkv_paged_attn_decode_noalloc: a fixed device array in this
+// library's code object, one copy per GPU that loads it, held until the
+// process ends. Its first PKV_NOALLOC_COUNTERS int32 are the ticket and
+// arrival counters (zero before a call, and every call leaves the arrival
+// counters at zero again); the PKV_NOALLOC_WORKSPACE_BYTES after them take
+// the split partials. In host code `scratch` names a host-side stand-in, never
+// the device memory: kernels and copies get the address hipGetSymbolAddress
+// returns for the current device (scratch_base).
+constexpr size_t kScratchCounterBytes = (size_t)PKV_NOALLOC_COUNTERS * sizeof(int32_t);
+constexpr size_t kScratchBytes = kScratchCounterBytes + (size_t)PKV_NOALLOC_WORKSPACE_BYTES;
+static_assert(kScratchCounterBytes % 256 == 0, "workspace part stays 256-byte aligned");
+static __device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+char *g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of the current device's scratch. The first call on a device
+// looks it up and clears the counters with a fill kernel on `stream`, ahead
+// of that call's own kernels (no allocation, no memset node).
+int scratch_base(hipStream_t stream, char **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxScratchDevices) return fail(PKV_ERR_DEVICE, "device %d: no scratch slot", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return hip_fail(e, "hipGetSymbolAddress (decode scratch)");
+    e = pkv::launch_zero_i32(static_cast<int32_t *>(p), PKV_NOALLOC_COUNTERS, stream);
+    if (e != hipSuccess) return hip_fail(e, "clearing the decode scratch counters");
+    g_scratch_ptr[dev] = static_cast<char *>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -210,7 +248,7 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
                 int32_t n_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_seqs,
                 int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype, void *stream, bool fp8,
                 const float *k_scale, const float *v_scale, const void *k_new = nullptr,
-                const void *v_new = nullptr) {
+                const void *v_new = nullptr, bool no_alloc = false) {
   if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID, "unknown dtype %d", dtype);
   if (fp8 && dtype == PKV_F32)
     return fail(PKV_ERR_UNSUPPORTED, "FP8 pools need a float16 or bfloat16 query and output");
@@ -283,11 +321,29 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
   const size_t ws_bytes = acc_bytes + rows * sizeof(float2);
   int32_t *counters = nullptr;
   void *ws = nullptr;
-  int rc = get_arrivals(st, counter_ints, &counters);
-  if (rc != PKV_OK) return rc;
-  if (rows) {
-    rc = get_workspace(st, ws_bytes, &ws);
+  if (no_alloc) {
+    if (counter_ints > PKV_NOALLOC_COUNTERS)
+      return fail(PKV_ERR_INVALID,
+                  "no-allocation decode: %lld merge counters needed (sequences x KV heads x head chunks + %lld), "
+                  "the scratch holds %d",
+                  (long long)counter_ints, (long long)kTicketInts, PKV_NOALLOC_COUNTERS);
+    if (ws_bytes > (size_t)PKV_NOALLOC_WORKSPACE_BYTES)
+      return fail(PKV_ERR_INVALID,
+                  "no-allocation decode: %zu bytes of split partials needed (%zu rows x (head_dim + 2) x 4), "
+                  "the scratch holds %zu",
+                  ws_bytes, rows, (size_t)PKV_NOALLOC_WORKSPACE_BYTES);
+    char *base = nullptr;
+    int rc = scratch_base(st, &base);
     if (rc != PKV_OK) return rc;
+    counters = reinterpret_cast<int32_t *>(base);
+    ws = base + kScratchCounterBytes;
+  } else {
+    int rc = get_arrivals(st, counter_ints, &counters);
+    if (rc != PKV_OK) return rc;
+    if (rows) {
+      rc = get_workspace(st, ws_bytes, &ws);
+      if (rc != PKV_OK) return rc;
+    }
   }
   a.tickets = reinterpret_cast<uint32_t *>(counters);
   if (rows) {
@@ -314,6 +370,16 @@ int pkv_paged_attn_decode(void *out, const void *q, const void *k_pool, const vo
   return decode_impl(out, q, k_pool, v_pool, block_tables, seq_lens, scale, n_heads, n_kv_heads, head_dim,
                      block_size, num_seqs, max_blocks_per_seq, num_blocks, dtype, stream, false, nullptr,
                      nullptr);
+}
+
+int pkv_paged_attn_decode_noalloc(void *out, const void *q, const void *k_pool, const void *v_pool,
+                                  const int32_t *block_tables, const int32_t *seq_lens, float scale,
+                                  int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t num_seqs, int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
+                                  void *stream) {
+  return decode_impl(out, q, k_pool, v_pool, block_tables, seq_lens, scale, n_heads, n_kv_heads, head_dim,
+                     block_size, num_seqs, max_blocks_per_seq, num_blocks, dtype, stream, false, nullptr,
+                     nullptr, nullptr, nullptr, true);
 }
 
 int pkv_paged_attn_decode_append(void *out, const void *q, void *k_pool, void *v_pool, const void *k_new,

@@ -119,3 +119,25 @@ def test_partition_plan():
 
 def test_version():
     assert _lib.version() >> 16 == 1
+
+
+def _decode_noalloc(**over):
+    args = dict(out=16, q=16, k_pool=16, v_pool=16, block_tables=16, seq_lens=16, scale=0.125,
+                n_heads=32, n_kv_heads=8, head_dim=128, block_size=16, num_seqs=4,
+                max_blocks_per_seq=8, num_blocks=64, dtype=2, stream=None)
+    args.update(over)
+    return _lib.lib().pkv_paged_attn_decode_noalloc(*args.values())
+
+
+def test_noalloc_decode_rejects_sizes_past_its_scratch():
+    """The no-allocation decode checks its fixed scratch before any HIP call:
+    too many split partials (300 sequences x 32 heads x 16 partitions x 130
+    floats = 80 MB > 64 MiB) or too many merge counters (3000 sequences x 8
+    KV heads > 16384 - 64) give PKV_ERR_INVALID with a message naming the
+    limit; the argument checks of the allocating call apply as well."""
+    assert _decode_noalloc(num_seqs=300, max_blocks_per_seq=1024) == _lib.PKV_ERR_INVALID
+    assert "split partials" in _lib.last_error()
+    assert _decode_noalloc(num_seqs=3000, n_heads=8, max_blocks_per_seq=80) == _lib.PKV_ERR_INVALID
+    assert "merge counters" in _lib.last_error()
+    assert _decode_noalloc(head_dim=96) == _lib.PKV_ERR_UNSUPPORTED
+    assert _decode_noalloc(num_seqs=0, q=None, out=None) == _lib.PKV_OK
