@@ -68,11 +68,12 @@ def log(msg):
 
 def stream_ceiling(device, nbytes=2 * 2 ** 30, iters=10):
     """Measured read ceilings (the library's probe kernels, pkv_probe.h) over
-    a 2 GiB buffer, 8x the memory-side cache: a sequential non-temporal read,
-    and a gather of 4 KiB tiles in shuffled order (the decode kernel's
-    pattern: one tile = one 16-token block of one KV head) at 1, 2 and 4 tiles
-    in flight per wave and two grid sizes; the best gather is reported with its
-    configuration. HIP events on the stream the probes run on."""
+    a 2 GiB buffer, 8x the memory-side cache: a grid-stride non-temporal read,
+    4 KiB tiles read in address order, and 4 KiB tiles in shuffled order (the
+    decode kernel's pattern: one tile = one 16-token block of one KV head),
+    the tile reads at 1, 2 and 4 tiles in flight per wave and two grid sizes
+    (the best is reported with its configuration); and torch's device copy of
+    the buffer (read + write bytes). HIP events on the stream they run on."""
     stream = torch.cuda.current_stream(device)
     buf = torch.empty(nbytes // 4, dtype=torch.int32, device=device).random_()
     cus = torch.cuda.get_device_properties(device).multi_processor_count
@@ -90,15 +91,23 @@ def stream_ceiling(device, nbytes=2 * 2 ** 30, iters=10):
         return nbytes * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
     res = {"stream_read": round(timed(lambda: _lib.probe_stream_read(buf, 8 * cus, sink, stream=stream)), 1)}
-    best = (0.0, None)
-    for depth in (1, 2, 4):
-        for per_cu in (8, 16):
-            g = timed(lambda: _lib.probe_gather_tiles(buf, tiles, depth, per_cu * cus, sink, stream=stream))
-            if g > best[0]:
-                best = (g, f"{depth} tiles in flight per wave, {per_cu} workgroups of 4 waves per CU")
-    res["gather_4k_tiles"] = round(best[0], 1)
-    res["gather_config"] = best[1]
+    seq = torch.arange(nbytes // 4096, device=device, dtype=torch.int32)
+    for name, order in (("sequential_4k_tiles", seq), ("gather_4k_tiles", tiles)):
+        best = (0.0, None)
+        for depth in (1, 2, 4):
+            for per_cu in (8, 16):
+                g = timed(lambda: _lib.probe_gather_tiles(buf, order, depth, per_cu * cus, sink, stream=stream))
+                if g > best[0]:
+                    best = (g, f"{depth} tiles in flight per wave, {per_cu} workgroups of 4 waves per CU")
+        res[name] = round(best[0], 1)
+        res[name + "_config"] = best[1]
+    # a plain device copy of the same buffer (read + write): the counter
+    # summaries under profiles/ scale FETCH_SIZE and WRITE_SIZE by what this
+    # copy of known size reads on them
+    dst = torch.empty_like(buf)
+    res["device_copy_rw"] = round(2 * timed(lambda: dst.copy_(buf)), 1)
     res["buffer_bytes"] = nbytes
+    del seq, dst
     del buf, tiles, sink
     torch.cuda.empty_cache()
     return res
@@ -458,9 +467,20 @@ def main():
         step(i % R, evs[i])
     torch.cuda.synchronize()
     dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    # the cache-write kernel alone (one new token per sequence), back to back
+    # The cache-write kernel alone (one new token per sequence), back to back.
+    # It runs for a few microseconds, less than the host takes to submit a
+    # call, so the calls are queued behind ~6 ms of probe reads (16 passes
+    # over 2 GiB): the GPU then runs them without waiting for the host, and
+    # the figure is the kernels' own (the host's submit time is printed
+    # beside it as a check).
     n_w = 200
+    blk = torch.empty(2 ** 29, dtype=torch.int32, device=dev)
+    sink = torch.zeros(8 * torch.cuda.get_device_properties(dev).multi_processor_count, dtype=torch.int32,
+                       device=dev)
     w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(16):
+        _lib.probe_stream_read(blk, sink.numel(), sink, stream=stream)
+    h0 = time.perf_counter()
     w0.record(stream)
     for i in range(n_w):
         if fp8:
@@ -468,8 +488,10 @@ def main():
         else:
             _lib.kv_cache_write(kps[i % R], vps[i % R], kn, vn, slots, stream=stream)
     w1.record(stream)
+    submit_us = (time.perf_counter() - h0) * 1e6 / n_w
     torch.cuda.synchronize()
     write_us = w0.elapsed_time(w1) * 1e3 / n_w
+    del blk, sink
 
     # compulsory bytes: K/V of each distinct cached token slot once (blocks that
     # several tables share, as in the shared-prompt workload, count once), Q, O
@@ -538,8 +560,9 @@ def main():
                      "algorithmic_bytes": int(call_bytes), "call_us": round(call_ms * 1e3, 3)},
         "wall_ms_per_step": round(wall * 1e3 / K, 5),
         "settle_steps": settle_steps,
-        "write_kernel_us": {"us": round(write_us, 3), "tokens": n_written,
-                            "note": f"kv_cache_write{'_fp8' if fp8 else ''} alone, {n_w} calls back to back"},
+        "write_kernel_us": {"us": round(write_us, 3), "tokens": n_written, "host_submit_us": round(submit_us, 2),
+                            "note": f"kv_cache_write{'_fp8' if fp8 else ''} alone, {n_w} calls queued behind "
+                                    f"probe reads and run back to back"},
     }
     if not args.no_ceiling:
         log("[bench] read ceilings (probe kernels)")

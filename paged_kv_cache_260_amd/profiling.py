@@ -88,8 +88,18 @@ def read_counter(path, counter):
     return per
 
 
+def read_trace(path):
+    """{kernel short name: [duration ns per dispatch, in dispatch order]}."""
+    per = defaultdict(list)
+    with open(path) as f:
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
+    for r in rows:
+        per[short_name(r["Kernel_Name"])].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return per
+
+
 def summarize(name, command, stats_csv, fetch_csv, write_csv, algorithmic_bytes, copy_bytes, out,
-              fetch_command=None, write_command=None):
+              fetch_command=None, write_command=None, trace_csv=None, skip=0, take=0):
     os.makedirs(out, exist_ok=True)
     stats = read_stats(stats_csv)
     lines = [f"# {name}: rocprofv3 kernel statistics", "", "Command (repository root):", "",
@@ -99,12 +109,32 @@ def summarize(name, command, stats_csv, fetch_csv, write_csv, algorithmic_bytes,
     for r in stats:
         lines.append(f"| {short_name(r['name'])} | {r['calls']} | {r['avg_ns'] / 1e3:.2f} | "
                      f"{r['min_ns'] / 1e3:.2f} | {r['max_ns'] / 1e3:.2f} | {r['pct']:.1f} |")
+    timed = {}
+    if trace_csv and take > 0:
+        # the statistics above average every call, warm-up included (the clocks
+        # ramp up during the first tens of milliseconds); the benchmark's figure
+        # comes from the calls it times, dispatches [skip, skip + take) of each
+        # kernel in the same trace
+        trace = read_trace(trace_csv)
+        lines += ["", f"Calls the benchmark times (dispatches {skip} to {skip + take - 1} of each kernel, "
+                  f"from the kernel trace of the same run):", "",
+                  "| kernel | calls | avg us | median us | min us | max us |", "|---|---|---|---|---|---|"]
+        for k, durs in trace.items():
+            win = sorted(durs[skip:skip + take])
+            if len(win) < take:
+                continue
+            avg = sum(win) / len(win)
+            timed[k] = avg / 1e3
+            lines.append(f"| {k} | {len(win)} | {avg / 1e3:.2f} | {win[len(win) // 2] / 1e3:.2f} | "
+                         f"{win[0] / 1e3:.2f} | {win[-1] / 1e3:.2f} |")
     with open(os.path.join(out, f"{name}_kernel_stats.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
     result = {"name": name, "decode_source_hash": source_hash(), "command": command,
               "algorithmic_bytes": int(algorithmic_bytes),
               "kernel_avg_us": {short_name(r["name"]): r["avg_ns"] / 1e3 for r in stats}}
+    if timed:
+        result["timed_calls_avg_us"] = timed
     if fetch_csv and write_csv:
         fetch = read_counter(fetch_csv, "FETCH_SIZE")
         write = read_counter(write_csv, "WRITE_SIZE")
@@ -152,7 +182,102 @@ def summarize(name, command, stats_csv, fetch_csv, write_csv, algorithmic_bytes,
     return result
 
 
+# Hardware counters read in the counter passes, with what they count (per
+# dispatch, summed over the chip by rocprofv3).
+COUNTER_NOTES = {
+    "SQ_WAVES": "waves launched",
+    "SQ_INSTS_VALU": "vector ALU instructions issued (wave level; MFMA included)",
+    "SQ_INSTS_MFMA": "MFMA instructions issued",
+    "SQ_INSTS_LDS": "LDS instructions issued",
+    "SQ_INSTS_VMEM_RD": "vector memory read instructions",
+    "SQ_INSTS_VMEM_WR": "vector memory write instructions",
+    "SQ_INSTS_SALU": "scalar ALU instructions",
+    "SQ_INSTS_VALU_MFMA_MOPS_BF16": "bf16 MFMA work in units of 512 flops",
+    "SQ_INSTS_VALU_MFMA_MOPS_F16": "fp16 MFMA work in units of 512 flops",
+    "SQ_WAVE_CYCLES": "wave-cycles resident (summed over waves)",
+    "SQ_BUSY_CYCLES": "cycles the sequencers had work",
+    "SQ_WAIT_ANY": "wave-cycles waiting for anything",
+    "SQ_WAIT_INST_ANY": "wave-cycles waiting for an instruction's dependency (memory data, mostly)",
+    "SQ_ACTIVE_INST_VALU": "wave-cycles issuing VALU instructions",
+    "SQ_ACTIVE_INST_ANY": "wave-cycles issuing any instruction",
+    "SQ_VALU_MFMA_BUSY_CYCLES": "SIMD-cycles the matrix cores were busy",
+    "SQ_LDS_BANK_CONFLICT": "cycles lost to LDS bank conflicts",
+    "SQ_LDS_IDX_ACTIVE": "cycles the LDS was processing indexed accesses",
+    "SQ_ACTIVE_INST_LDS": "wave-cycles issuing LDS instructions",
+    "SQ_ACTIVE_INST_VMEM": "wave-cycles issuing vector memory instructions",
+    "SQ_INST_LEVEL_VMEM": "vector memory instructions in flight, summed per cycle",
+    "GRBM_GUI_ACTIVE": "GPU-busy cycles (elapsed clock)",
+}
+
+
+def counters(name, kernel, commands, csvs, out, units=None, unit_name=None, simds=1024, xcds=8, skip_first=1):
+    """Summary of counter passes (one CSV per rocprofv3 --pmc run) for the
+    dispatches of `kernel` (a short name as short_name gives it): the average
+    of each counter per dispatch, and ratios that say what bounds the kernel."""
+    vals = {}
+    for path in csvs:
+        with open(path) as f:
+            rows = sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
+        per = defaultdict(list)
+        for r in rows:
+            if short_name(r["Kernel_Name"]) == kernel:
+                per[r["Counter_Name"]].append(float(r["Counter_Value"]))
+        for c, v in per.items():
+            v = v[skip_first:] or v
+            vals[c] = sum(v) / len(v)
+    g = lambda c: vals.get(c)
+    lines = [f"# {name}: hardware counters of `{kernel}`", "",
+             "Counter passes (repository root), one rocprofv3 run each:", "", "```", *commands, "```", "",
+             f"Averages per dispatch (the first dispatch skipped), {len(vals)} counters:", "",
+             "| counter | per dispatch | what it counts |", "|---|---|---|"]
+    for c in sorted(vals):
+        lines.append(f"| {c} | {vals[c]:.4g} | {COUNTER_NOTES.get(c, '')} |")
+    derived = []
+
+    def ratio(label, num, den, scale=1.0, fmt="{:.3g}"):
+        if num is not None and den:
+            derived.append((label, fmt.format(scale * num / den)))
+
+    # GRBM_GUI_ACTIVE comes summed over the XCDs: per XCD it is the elapsed clock
+    ratio("elapsed us at 2.4 GHz (GRBM_GUI_ACTIVE per XCD)", g("GRBM_GUI_ACTIVE"), xcds * 2400.0)
+    ratio("MFMA busy, % of SIMD-cycles", g("SQ_VALU_MFMA_BUSY_CYCLES"),
+          (g("GRBM_GUI_ACTIVE") or 0) / xcds * simds, 100.0)
+    ratio("VALU issue, % of resident wave-cycles", g("SQ_ACTIVE_INST_VALU"), g("SQ_WAVE_CYCLES"), 100.0)
+    ratio("any issue, % of resident wave-cycles", g("SQ_ACTIVE_INST_ANY"), g("SQ_WAVE_CYCLES"), 100.0)
+    ratio("waiting on a dependency, % of resident wave-cycles", g("SQ_WAIT_INST_ANY"), g("SQ_WAVE_CYCLES"), 100.0)
+    ratio("LDS bank-conflict cycles, % of LDS-active cycles", g("SQ_LDS_BANK_CONFLICT"), g("SQ_LDS_IDX_ACTIVE"), 100.0)
+    ratio("MFMA share of VALU instructions, %", g("SQ_INSTS_MFMA"), g("SQ_INSTS_VALU"), 100.0)
+    ratio("vector memory instructions in flight (average)", g("SQ_INST_LEVEL_VMEM"), g("SQ_ACTIVE_INST_VMEM"))
+    if units:
+        for c in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD"):
+            ratio(f"{c} per {unit_name}", g(c), units)
+        mops = (g("SQ_INSTS_VALU_MFMA_MOPS_BF16") or 0) + (g("SQ_INSTS_VALU_MFMA_MOPS_F16") or 0)
+        if mops:
+            derived.append((f"MFMA flops per {unit_name}", f"{512 * mops / units:.4g}"))
+    if derived:
+        lines += ["", "| derived | value |", "|---|---|"] + [f"| {a} | {b} |" for a, b in derived]
+    os.makedirs(out, exist_ok=True)
+    with open(os.path.join(out, f"{name}_counters.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return vals, derived
+
+
 def main():
+    import sys
+    if len(sys.argv) > 1 and sys.argv[1] == "counters":
+        ap = argparse.ArgumentParser()
+        ap.add_argument("cmd")
+        ap.add_argument("--name", required=True)
+        ap.add_argument("--kernel", required=True)
+        ap.add_argument("--csv", action="append", required=True)
+        ap.add_argument("--command", action="append", required=True)
+        ap.add_argument("--units", type=float)
+        ap.add_argument("--unit-name")
+        ap.add_argument("--out", required=True)
+        a = ap.parse_args()
+        vals, derived = counters(a.name, a.kernel, a.command, a.csv, a.out, a.units, a.unit_name)
+        print(json.dumps({"counters": vals, "derived": dict(derived)}))
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--name", required=True)
     ap.add_argument("--command", required=True)
@@ -164,9 +289,12 @@ def main():
     ap.add_argument("--out", required=True)
     ap.add_argument("--fetch-command")
     ap.add_argument("--write-command")
+    ap.add_argument("--trace", help="kernel trace CSV of the statistics run")
+    ap.add_argument("--skip", type=int, default=0, help="untimed calls before the timed ones")
+    ap.add_argument("--take", type=int, default=0, help="timed calls")
     a = ap.parse_args()
     r = summarize(a.name, a.command, a.stats, a.fetch, a.write, a.algorithmic_bytes, a.copy_bytes,
-                  a.out, a.fetch_command, a.write_command)
+                  a.out, a.fetch_command, a.write_command, a.trace, a.skip, a.take)
     print(json.dumps(r))
 
 
