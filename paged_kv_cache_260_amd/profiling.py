@@ -58,7 +58,7 @@ _DECODE_MODES = {"0": "", "1": " (chunk rows)", "2": " (shared prefix)", "3": " 
 def short_name(name: str) -> str:
     for key in (*CALL_KERNELS, "paged_chunk_reduce_kernel", "paged_chunk_kernel", "kv_cache_write_fp8_kernel",
                 "kv_cache_write_kernel",
-                "zero_i32_kernel", "copy_blocks_kernel", COPY_KERNEL):
+                "zero_i32_kernel", "copy_blocks_kernel", "stream_read_kernel", "gather_tiles_kernel", COPY_KERNEL):
         if key in name:
             if key == DECODE_KERNEL and name.endswith("EEEvNS_10DecodeArgsE") and "ELi" in name:
                 mode = name[: -len("EEEvNS_10DecodeArgsE")].rsplit("ELi", 1)[-1]
@@ -245,6 +245,10 @@ def counters(name, kernel, commands, csvs, out, units=None, unit_name=None, simd
     ratio("VALU issue, % of resident wave-cycles", g("SQ_ACTIVE_INST_VALU"), g("SQ_WAVE_CYCLES"), 100.0)
     ratio("any issue, % of resident wave-cycles", g("SQ_ACTIVE_INST_ANY"), g("SQ_WAVE_CYCLES"), 100.0)
     ratio("waiting on a dependency, % of resident wave-cycles", g("SQ_WAIT_INST_ANY"), g("SQ_WAVE_CYCLES"), 100.0)
+    ratio("waiting for anything (dependencies, barriers), % of resident wave-cycles", g("SQ_WAIT_ANY"),
+          g("SQ_WAVE_CYCLES"), 100.0)
+    ratio("LDS busy with indexed accesses, % of CU-cycles", g("SQ_LDS_IDX_ACTIVE"),
+          (g("GRBM_GUI_ACTIVE") or 0) / xcds * (simds // 4), 100.0)
     ratio("LDS bank-conflict cycles, % of LDS-active cycles", g("SQ_LDS_BANK_CONFLICT"), g("SQ_LDS_IDX_ACTIVE"), 100.0)
     ratio("MFMA share of VALU instructions, %", g("SQ_INSTS_MFMA"), g("SQ_INSTS_VALU"), 100.0)
     ratio("vector memory instructions in flight (average)", g("SQ_INST_LEVEL_VMEM"), g("SQ_ACTIVE_INST_VMEM"))

@@ -109,6 +109,21 @@ def test_prefill_chunks(H, Hkv, D, BS, dtype):
     assert max_abs_err(out, run_oracle(w, q, qsl)) <= TOL[dtype]
 
 
+def test_prefill_benchmark_shape():
+    """The prefill workload the benchmark times, every output row: 4 sequences
+    of 4 096 cached tokens, each scoring its last 512 tokens as one chunk (GQA
+    32/8, head_dim 128, block 16, bf16): 8 row blocks of 256 rows per KV head,
+    64 stages of 64 context tokens."""
+    say("prefill chunks at the benchmark shape: 4 x 512 of 4096")
+    w = workloads.build(name="prefill", rng=np.random.default_rng(2607), seq_lens=np.full(4, 4096), n_heads=32,
+                        n_kv_heads=8, head_dim=128, block_size=16, dtype=torch.bfloat16, poison=True)
+    q, qsl = chunk_inputs(w, np.full(4, 512), 7)
+    out = run_gpu(w, q, qsl)
+    err = max_abs_err(out, run_oracle(w, q, qsl))
+    say(f"  max abs err {err:.3e}")
+    assert err <= TOL[w.dtype]
+
+
 def test_whole_sequence_prefill_and_mixed_batch():
     """Whole-sequence chunks, decode steps and empty chunks in one batch."""
     w = workloads.random_case(31, num_seqs=6, n_heads=16, n_kv_heads=4, head_dim=128, block_size=16,
