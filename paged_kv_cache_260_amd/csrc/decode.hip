@@ -66,11 +66,16 @@ constexpr int kRemBuckets = 8;
 //         batch). compact_plan keeps incl below 2^23.
 //   cnt:  per (bucket b, chunk c) entity counts at b * 4 + c, then the chunks'
 //         full-partition totals at 36 + c;
-//   aux:  shared mode, the chunks' longest private parts.
+//   aux:  shared mode, the chunks' longest private parts;
+//   chg:  shared mode, per entity one bit: its sequence's prefix length
+//         differs from the previous sequence's (64 bits per chunk);
+//   bad:  shared mode, per chunk: a group of the chunk breaks the description.
 constexpr int kPlanEntry = 0;
 constexpr int kPlanCnt = kCompactSeqs;
 constexpr int kPlanAux = kPlanCnt + (kRemBuckets + 1) * kCompactChunks + kCompactChunks;
-constexpr int kPlanTicket = kPlanAux + kCompactChunks;  // a late workgroup's ticket
+constexpr int kPlanChg = kPlanAux + kCompactChunks;
+constexpr int kPlanBad = kPlanChg + 2 * kCompactChunks;
+constexpr int kPlanTicket = kPlanBad + kCompactChunks;  // a late workgroup's ticket
 constexpr int kPlanInts = kPlanTicket + 1;
 static_assert(kDecodeWaves == kCompactChunks, "one wave per 64-entity chunk of the plan");
 static_assert((kRemBuckets + 1) * kCompactChunks <= 64, "bucket counts fit one wave");
@@ -228,36 +233,51 @@ __device__ __forceinline__ void make_plan(const DecodeArgs &a, ItemPlan &pl, int
     const int m = min(max(first, 0), a.member_seqs - 1);
     const int len = a.seq_lens[m];
     const int pre = a.prefix_lens[m];
+    // a private lane also reads the previous sequence's prefix length (its
+    // own index is known, so this load goes out with the first ones)
+    const int pre_prev = !is_pre && m > 0 ? a.prefix_lens[m - 1] : pre;
     // The arrival counts of the prefix and private partitions of a sequence
     // agree only if the description holds: the groups cut [0, member_seqs)
     // into consecutive ranges of at most kSharedRows / group members, and a
     // group's members share one prefix length. Each group lane checks its own
-    // range and members; one violation anywhere makes the whole call write
-    // NaN rows and count no arrivals, so the counters stay at zero.
+    // range here, and after the first barrier that no private lane inside it
+    // saw the prefix length change from the sequence before; one violation
+    // anywhere makes the whole call write NaN rows and count no arrivals, so
+    // the counters stay at zero.
     bool bad = false;
     if (in && is_pre) {
       const int nmem = gend - first;
       bad = first < 0 || nmem < 1 || gend > a.member_seqs || nmem * a.group > kSharedRows ||
             (e == 0 && first != 0) || (e == ng - 1 && gend != a.member_seqs);
-      int mp[kSharedRows - 1];
-#pragma unroll
-      for (int k = 0; k < kSharedRows - 1; ++k) mp[k] = a.prefix_lens[min(m + 1 + k, a.member_seqs - 1)];
-#pragma unroll
-      for (int k = 0; k < kSharedRows - 1; ++k) bad |= k + 1 < nmem && mp[k] != pre;
     }
+    const unsigned long long chg = __builtin_amdgcn_ballot_w64(in && !is_pre && pre_prev != pre);
     L = is_pre ? pre : (pre >= 0 && pre <= len ? len - pre : -1);
     int max_private = !is_pre && in && (int64_t)len <= max_tok ? max(L, 0) : 0;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) max_private = max(max_private, __shfl_xor(max_private, d, 64));
-    const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0ull;  // every lane votes (outside the branch)
-    if (lane == 0) sp[kPlanAux + c] = wave_bad ? -1 : max_private;
+    if (lane == 0) {
+      sp[kPlanAux + c] = max_private;
+      sp[kPlanChg + 2 * c] = (int)(uint32_t)chg;
+      sp[kPlanChg + 2 * c + 1] = (int)(uint32_t)(chg >> 32);
+    }
     __syncthreads();
 #pragma unroll
-    for (int cc = 0; cc < kCompactChunks; ++cc) {
-      const int v = sp[kPlanAux + cc];
-      pl.bad_desc |= v < 0;
-      max_private = max(max_private, v);
+    for (int cc = 0; cc < kCompactChunks; ++cc) max_private = max(max_private, sp[kPlanAux + cc]);
+    if (in && is_pre && !bad) {
+      // change bits of entities ng + first + 1 .. ng + gend - 1 (at most 15,
+      // within two consecutive words of the bit array)
+      const int b0 = ng + first + 1, b1 = ng + gend;  // [b0, b1), b1 <= kCompactSeqs
+      if (b1 > b0) {
+        const int wi = b0 >> 5;
+        const uint64_t lo = (uint32_t)sp[kPlanChg + wi];
+        const uint64_t hi = wi + 1 < 2 * kCompactChunks ? (uint32_t)sp[kPlanChg + wi + 1] : 0u;
+        const uint64_t w = lo | (hi << 32);
+        const uint64_t mask = ((1ull << (b1 - b0)) - 1ull) << (b0 & 31);  // b1 - b0 <= 15
+        bad = (w & mask) != 0ull;
+      }
     }
+    const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0ull;  // every lane votes (outside the branch)
+    if (lane == 0) sp[kPlanBad + c] = wave_bad ? 1 : 0;
     pl.p_pre = __builtin_amdgcn_readfirstlane(shared_prefix_partition(a, max_private));
     Pe = is_pre ? pl.p_pre : P;
   } else if constexpr (MODE == kModePrefix) {
@@ -308,6 +328,10 @@ __device__ __forceinline__ void make_plan(const DecodeArgs &a, ItemPlan &pl, int
   __syncthreads();
   pl.full_items = __builtin_amdgcn_readfirstlane(ftot);
   pl.items = pl.full_items + B;
+  if constexpr (MODE == kModeShared) {
+#pragma unroll
+    for (int cc = 0; cc < kCompactChunks; ++cc) pl.bad_desc |= sp[kPlanBad + cc] != 0;
+  }
 }
 
 // Item j (< pl.items) of the order above -> (entity, partition), uniform:
@@ -466,16 +490,12 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
       q0 = s - a.num_groups;
       nq = 1;
     }
-    bad_rows = q0 < 0 || nq < 1 || q0 + nq > a.member_seqs;
-    if (bad_desc) {
-      // the sharing description is broken (make_plan): each sequence's first
-      // private item writes its NaN rows, nothing else runs or counts
-      if (!pre_item && part == 0 && !bad_rows) {
-        for (int i = tid; i < min(GT, G) * D; i += kNW * 64)
-          out[((int64_t)q0 * H + g * G + i / D) * D + i % D] = static_cast<T>(__builtin_nanf(""));
-      }
-      return;
-    }
+    // a broken sharing description (make_plan): prefix items get no rows,
+    // private items take the invalid-length path below (NaN rows, written by
+    // each sequence's first private item); nothing counts an arrival. (Both
+    // checks come after the item's first loads are issued: an early exit
+    // here measured 1.6 us slower on the prompt-samples batch.)
+    bad_rows = q0 < 0 || nq < 1 || q0 + nq > a.member_seqs || (pre_item && bad_desc);
   } else if constexpr (RM) {
     q0 = a.query_start_loc[s];
     nq = a.query_start_loc[s + 1] - q0;
@@ -578,7 +598,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   if constexpr (MODE == kModeSuffix) bad_len |= tok0 < 0 || tok0 > L || (tok0 & (a.block_size - 1)) != 0;
   if constexpr (SH) {
     if (pre_item) bad_len |= (L & (a.block_size - 1)) != 0;
-    else bad_len |= tok0 < 0 || tok0 > L || (tok0 & (a.block_size - 1)) != 0;
+    else bad_len |= tok0 < 0 || tok0 > L || (tok0 & (a.block_size - 1)) != 0 || bad_desc;
   }
   if constexpr (MODE == kModePrefix) {
     if (bad_len || L == 0) return;
