@@ -75,8 +75,34 @@ def pin_power_of_two_scale(mod):
     assert np.array_equal(mod.quantize(x, s), mod.encode(x / s[None, :, None].astype(np.float64)))
 
 
+def pin_exact_division_away_from_ties(mod):
+    """Any scale: the float32 steps the quantizer takes, fl32(x * fl32(1/s)),
+    stay within 2^-23 (relative) of the exact quotient x/s (two roundings of
+    at most 2^-24 each), so the code must be the nearest-e4m3 code of x/s
+    itself whenever x/s lies farther than 2^-21 (relative) from every point
+    where the nearest code changes (the midpoints between adjacent values,
+    and the saturation bound). Near such points the two may differ by one
+    code; they are a small minority of the samples."""
+    rng = np.random.default_rng(11)
+    v = mod.decode(np.arange(0x7F, dtype=np.uint8))
+    mids = (v[:-1] + v[1:]) / 2
+    s = np.array([0.0173, 0.3, 1.7, 3.14159, 47.0, 1e-3], dtype=np.float32)
+    x = np.concatenate([rng.normal(0, 1, (3000, len(s), 4)), rng.normal(0, 30, (3000, len(s), 4))]).astype(np.float32)
+    got = mod.quantize(x, s)
+    q = x.astype(np.float64) / s.astype(np.float64)[None, :, None]        # exact to 2^-53
+    exact = mod.encode(q)
+    a = np.abs(q)
+    near = np.min(np.abs(a[..., None] - mids), axis=-1) <= a * 2.0 ** -21
+    assert np.array_equal(got[~near], exact[~near])
+    assert near.mean() < 1e-3
+    # where they may differ, they differ by at most one code of the same sign
+    dv = np.abs(mod.decode(got[near]) - mod.decode(exact[near]))
+    step = np.abs(mod.decode(exact[near])) * 2.0 ** -2 + 2.0 ** -9
+    assert np.all(dv <= step)
+
+
 PINS = [pin_known_values, pin_round_trip, pin_ties_and_saturation, pin_error_bound,
-        pin_scalar_equals_vector, pin_power_of_two_scale]
+        pin_scalar_equals_vector, pin_power_of_two_scale, pin_exact_division_away_from_ties]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -92,6 +118,9 @@ MUTANTS = {
     "scale multiplied": ("inv = (np.float32(1.0) / np.asarray(scale, dtype=np.float32))",
                          "inv = (np.float32(1.0) * np.asarray(scale, dtype=np.float32))"),
     "sign dropped": ("code = np.where(np.isnan(v), 0x7F, code) | sign", "code = np.where(np.isnan(v), 0x7F, code)"),
+    "reciprocal in half precision": ("inv = (np.float32(1.0) / np.asarray(scale, dtype=np.float32)).astype(np.float32)",
+                                     "inv = (np.float32(1.0) / np.asarray(scale, dtype=np.float32)).astype(np.float16)"
+                                     ".astype(np.float32)"),
 }
 
 
