@@ -231,6 +231,7 @@ void paged_chunk_kernel(ChunkArgs a) {
     sl2 *= a.k_scale[g];
     vsc = a.v_scale[g];
   }
+  const float inv_sl2 = 1.f / sl2;
   // transposed V reads: this lane addresses token 4 kg + (n >> 2) of a 16-token block
   const int tr_tok = 4 * kg + (n >> 2);
   const int v_tr_off = tr_tok * kCh * 16 + (lane & 3) * 8;
@@ -260,15 +261,9 @@ void paged_chunk_kernel(ChunkArgs a) {
       }
     }
     u32x4_t pt[2][2];  // P^T operands: [row tile][32-token half]
-    float z[2][4][4];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) z[rt][tb][r] = sc[tb][rt][r] * sl2;
-    // causal mask, only in the stages that reach past a row's position (a
-    // real branch: the empty asm keeps it from becoming selects everywhere)
+    // raw scores (the scale is applied inside the exponent's FMA); the causal
+    // mask, only in the stages that reach past a row's position (a real
+    // branch: the empty asm keeps it from becoming selects everywhere)
     if (t0 + kPfStage - 1 > wave_min_pos) {
       asm volatile("");
 #pragma unroll
@@ -277,24 +272,27 @@ void paged_chunk_kernel(ChunkArgs a) {
         for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            z[rt][tb][r] = t0 + tb * 16 + 4 * kg + r <= rpos[rt] ? z[rt][tb][r] : -INFINITY;
+            sc[tb][rt][r] = t0 + tb * 16 + 4 * kg + r <= rpos[rt] ? sc[tb][rt][r] : -INFINITY;
     }
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
+      // a raw score passes the reference by more than kLazy (base-2 units)
+      // when it exceeds (m + kLazy) / sl2 (sl2 > 0)
+      const float thr = (m[rt] + kLazy) * inv_sl2;
       bool over = false;
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) over |= z[rt][tb][r] > m[rt] + kLazy;
+        for (int r = 0; r < 4; ++r) over |= sc[tb][rt][r] > thr;
       if (__builtin_amdgcn_ballot_w64(over) != 0) {  // uniform: raise the reference
-        float mx = z[rt][0][0];
+        float mx = sc[0][rt][0];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, z[rt][tb][r]);
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[tb][rt][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mn = fmaxf(m[rt], mx);
+        const float mn = fmaxf(m[rt], mx * sl2);
         const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[rt] - mn);
         m[rt] = mn;
         lsum[rt] *= alpha;
@@ -307,7 +305,7 @@ void paged_chunk_kernel(ChunkArgs a) {
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p[tb][r] = __builtin_amdgcn_exp2f(z[rt][tb][r] - m[rt]);
+        for (int r = 0; r < 4; ++r) p[tb][r] = __builtin_amdgcn_exp2f(fmaf(sc[tb][rt][r], sl2, -m[rt]));
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         pt[rt][h] = u32x4_t{pack2<T>(p[2 * h][0], p[2 * h][1]), pack2<T>(p[2 * h][2], p[2 * h][3]),
