@@ -1259,7 +1259,12 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   }
 }
 
-// Three workgroups per CU (12 waves) keep enough K/V loads in flight; the
+// Three workgroups per CU (12 waves). Bandwidth alone would not need them
+// (a gather of 4 KiB tiles reaches the chip's read rate with 2 workgroups of
+// 4 waves per CU, one tile in flight per wave), but every item also has
+// latency-bound phases (plan, first loads, merge), and more resident
+// workgroups keep more items streaming while others are in those phases:
+// 2 per CU measured 3% slower on the GQA batch-128 step, 1 per CU 28%. The
 // register budget is pinned so the item loop does not trade occupancy for
 // registers. fp32 storage with large head tiles needs more registers.
 // Waves per SIMD the register budget is set for: 16-bit pools 3 (at 4 the
