@@ -980,10 +980,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
           uint32_t d[4];
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
-            const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
-            const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
-            d[2 * i] = pack2_exact<T>(f01[0], f01[1]);
-            d[2 * i + 1] = pack2_exact<T>(f23[0], f23[1]);
+            d[2 * i] = fp8x2_to<T>(w[i], false);
+            d[2 * i + 1] = fp8x2_to<T>(w[i], true);
           }
           staged = u32x4_t{d[0], d[1], d[2], d[3]};
         }

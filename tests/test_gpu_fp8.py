@@ -284,3 +284,56 @@ def test_fp8_shared_prefix(case):
     err = max_abs_err(out, oracle_fp8(w, kc, vc, ks, vs))
     say(f"  max abs err {err:.3e}")
     assert err <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("append", [False, True])
+def test_fp8_decode_every_code_exact(dtype, append):
+    """Every one of the 256 e4m3 codes through the decode kernel's own
+    conversion, bit for bit: one token of each sequence dominates its softmax
+    by more than 300 (natural-log units, so the others weigh exactly 0 in
+    fp32), its V row holds 128 different codes and both scales are 1, so each
+    output element must be the code's value exactly (every e4m3 value is exact
+    in fp16 and bf16), NaN for the two NaN codes. The other tokens hold finite
+    codes. With `append` the one-call step (its new token is not the
+    dominant one) takes the same path."""
+    dev = "cuda"
+    B, H, Hkv, D, BS, L = 2, 1, 1, 128, 16, 40
+    jstar = [17, 33]
+    nb = B * ((L + BS) // BS + 1)
+    rng = np.random.default_rng(31)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    kc = np.zeros((nb, Hkv, BS, D), dtype=np.uint8)
+    vc = rng.choice(finite, size=(nb, Hkv, BS, D)).astype(np.uint8)
+    tables = np.arange(nb, dtype=np.int32).reshape(B, -1)
+    for s in range(B):
+        for j in range(L + 1):
+            blk, off = tables[s, j // BS], j % BS
+            kc[blk, 0, off, 0] = 0x7E if j == jstar[s] else 0xFE     # +448 / -448
+        blk, off = tables[s, jstar[s] // BS], jstar[s] % BS
+        vc[blk, 0, off, :] = np.arange(128 * s, 128 * s + 128, dtype=np.uint8)
+    q = torch.zeros((B, H, D), dtype=dtype)
+    q[:, :, 0] = 4.0
+    ones = torch.ones(Hkv, dtype=torch.float32, device=dev)
+    out = torch.full((B, H, D), float("nan"), dtype=dtype, device=dev)
+    kp, vp = torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev)
+    bt = torch.from_numpy(tables).to(dev)
+    scale = 1.0 / np.sqrt(D)
+    if append:
+        # the new token (position L) gets a -448 key: it never dominates
+        kn = torch.zeros((B, Hkv, D), dtype=dtype)
+        kn[:, :, 0] = -448.0
+        vn = torch.zeros((B, Hkv, D), dtype=dtype)
+        sl = torch.full((B,), L + 1, dtype=torch.int32, device=dev)
+        _lib.paged_attn_decode_append_fp8(out, q.to(dev), kp, vp, kn.to(dev), vn.to(dev), ones, ones, bt, sl, scale,
+                                          H, Hkv, D, BS)
+    else:
+        sl = torch.full((B,), L, dtype=torch.int32, device=dev)
+        _lib.paged_attn_decode_fp8(out, q.to(dev), kp, vp, ones, ones, bt, sl, scale, H, Hkv, D, BS)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().reshape(B, D)
+    want = ofp8.decode(np.arange(256, dtype=np.uint8)).reshape(B, D)
+    say(f"every-code decode {dtype} append={append}")
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])   # -0.0 == 0.0 here: the sum's sign of zero is not a code value
