@@ -141,3 +141,16 @@ def test_noalloc_decode_rejects_sizes_past_its_scratch():
     assert "merge counters" in _lib.last_error()
     assert _decode_noalloc(head_dim=96) == _lib.PKV_ERR_UNSUPPORTED
     assert _decode_noalloc(num_seqs=0, q=None, out=None) == _lib.PKV_OK
+
+
+def test_probe_kernels_reject_bad_arguments():
+    """The read-ceiling probes check their arguments before any HIP call."""
+    lib = _lib.lib()
+    assert lib.pkv_probe_stream_read(None, 4096, 1, 16, None) == _lib.PKV_ERR_INVALID
+    assert lib.pkv_probe_stream_read(16, 4095, 1, 16, None) == _lib.PKV_ERR_INVALID    # not whole 16-byte units
+    assert lib.pkv_probe_stream_read(8, 4096, 1, 16, None) == _lib.PKV_ERR_INVALID     # misaligned
+    assert lib.pkv_probe_stream_read(16, 4096, 0, 16, None) == _lib.PKV_ERR_INVALID    # empty grid
+    assert lib.pkv_probe_gather_tiles(16, 8, 16, 4, 3, 1, 16, None) == _lib.PKV_ERR_UNSUPPORTED  # depth 3
+    assert "depth" in _lib.last_error()
+    assert lib.pkv_probe_gather_tiles(16, 0, 16, 4, 1, 1, 16, None) == _lib.PKV_ERR_INVALID     # no tiles
+    assert lib.pkv_probe_gather_tiles(16, 8, None, 4, 1, 1, 16, None) == _lib.PKV_ERR_INVALID
