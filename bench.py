@@ -346,6 +346,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     _lib.lib()
+    _lib.set_partition_tokens(args.partition)   # every op that runs the decode kernel
     if args.op == "copy_blocks":
         bench_copy_blocks(args, dev)
         return
@@ -355,7 +356,6 @@ def main():
     if args.op == "shared_prefix":
         bench_shared_prefix(args, dev)
         return
-    _lib.set_partition_tokens(args.partition)
 
     log(f"[bench] building workload config {args.config}")
     w = workloads.make(args.config)
