@@ -728,6 +728,11 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   char *vst = wreg + C::kVstOff;
   char *pst = wreg + C::kPstOff;
   const u32x4_t *qs = reinterpret_cast<const u32x4_t *>(smem + C::kQOff);
+  // 16-bit pools keep the wave's Q operand in registers for the whole item
+  // (read from LDS once, after the workgroup has staged it) instead of
+  // reading it from LDS for every tile
+  constexpr bool kQReg = !F8 && C::kPvMfma;
+  u32x4_t qreg[kQReg ? C::kSteps : 1];
 
   // Running softmax state per head row: lanes (kg, n) own heads 4 kg + r.
   // m[r] is a reference max in base-2 units, uniform across the 16 lanes of
@@ -870,7 +875,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < C::kSteps; ++c)
-      sc = mfma_chunk<T>(n < GT ? qs[kst_slot<kCh>(n, kg + 4 * c)] : u32x4_t{0u, 0u, 0u, 0u},
+      sc = mfma_chunk<T>(kQReg ? qreg[kQReg ? c : 0] : (n < GT ? qs[kst_slot<kCh>(n, kg + 4 * c)] : u32x4_t{0u, 0u, 0u, 0u}),
                          kst[kst_slot<kCh>(n, kg + 4 * c)], sc);
 
     // scores in base-2 units; tokens past the sequence (chunk rows: past the
@@ -1031,6 +1036,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
     if (tid < 16) mtot[tid] = tid < nmem ? mem_tot : 0;
   }
   __syncthreads();
+  if constexpr (kQReg) {
+#pragma unroll
+    for (int c = 0; c < C::kSteps; ++c) qreg[c] = n < GT ? qs[kst_slot<kCh>(n, kg + 4 * c)] : u32x4_t{0u, 0u, 0u, 0u};
+  }
   // streaming runs at normal priority; the latency chains around it (plan,
   // item start, merge) run raised, so a SIMD's streaming waves do not hold
   // them up
