@@ -1,7 +1,8 @@
 // Device helpers shared by the paged attention kernels (decode and the
 // multi-token kernel): 16-byte chunk types, MFMA steps on one chunk per lane,
-// 16-lane DPP reductions, the transposed LDS read, the LDS swizzles of staged
-// K and V tiles, and the exact FP8 (OCP e4m3) decode into 16-bit chunks.
+// reductions across the four 16-lane rows of a wave, the transposed LDS read,
+// the LDS swizzles of staged K and V tiles, and the exact FP8 (OCP e4m3)
+// decode into 16-bit chunks.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -72,27 +73,40 @@ template <> __device__ __forceinline__ f32x4_t mfma_chunk<float>(u32x4_t a, u32x
   return c;
 }
 
-// ---------------------------------------------------------------------------
-// 16-lane (DPP row) reductions; every lane of the row receives the result
-// ---------------------------------------------------------------------------
-template <int kCtrl> __device__ __forceinline__ float dpp_f(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
+// Across the four 16-lane rows (lanes n, n + 16, n + 32, n + 48; every lane
+// receives the result): gfx950's row swaps, v_permlane16_swap (odd rows of
+// one register with even rows of the other) and v_permlane32_swap (upper
+// half of one with lower half of the other), applied to two copies of x, put
+// each lane's partner in one of the two registers. VALU only, no LDS round
+// trip. (The second copy is made opaque to the compiler, which otherwise
+// treats the two results of a swap of equal inputs as one value.)
+__device__ __forceinline__ void swap16(uint32_t &a, uint32_t &b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
 }
-// row_ror:n has control 0x120 + n; rotations by 8, 4, 2, 1 cover the row.
-__device__ __forceinline__ float row_max16(float x) {
-  x = fmaxf(x, dpp_f<0x128>(x));
-  x = fmaxf(x, dpp_f<0x124>(x));
-  x = fmaxf(x, dpp_f<0x122>(x));
-  x = fmaxf(x, dpp_f<0x121>(x));
-  return x;
+__device__ __forceinline__ void swap32(uint32_t &a, uint32_t &b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
 }
-__device__ __forceinline__ float row_sum16(float x) {
-  x += dpp_f<0x128>(x);
-  x += dpp_f<0x124>(x);
-  x += dpp_f<0x122>(x);
-  x += dpp_f<0x121>(x);
-  return x;
+__device__ __forceinline__ float cols_max4(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  asm volatile("" : "+v"(b));
+  swap16(a, b);
+  a = b = __builtin_bit_cast(uint32_t, fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b)));
+  asm volatile("" : "+v"(b));
+  swap32(a, b);
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+__device__ __forceinline__ float cols_sum4(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  asm volatile("" : "+v"(b));
+  swap16(a, b);
+  a = b = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b));
+  asm volatile("" : "+v"(b));
+  swap32(a, b);
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
 
 __device__ __forceinline__ float readlane_f(float x, int lane) {

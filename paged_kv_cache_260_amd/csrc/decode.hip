@@ -26,16 +26,17 @@
 //   2. Both go to wave-private LDS tiles (XOR-swizzled 16-byte chunks, bank
 //      conflict free for the writes and the operand reads); the registers
 //      then take the next tile's loads.
-//   3. Scores S[head][token] = Q (heads x D, rows padded to 16) * K^T come out
-//      of v_mfma_f32_16x16x32_{bf16,f16} (16x16x4 for fp32): lane (kg, n)
-//      receives heads 4kg..4kg+3 of token n.
+//   3. Transposed scores S^T[token][head] = K * Q^T (heads padded to 16) come
+//      out of v_mfma_f32_16x16x32_{bf16,f16} (16x16x4 for fp32): lane (kg, n)
+//      receives tokens 4kg..4kg+3 of head row n.
 //   4. Online softmax in base 2 (scale * log2 e folded into one multiply)
 //      against a reference max that is raised only when a score passes it by
-//      more than 8 (so every weight stays <= 2^8); only then are rows reduced
-//      with DPP and the sums rescaled.
-//   5. 16-bit storage: P (as hi + lo halves) and the V tile are read back
-//      transposed with ds_read_b64_tr_b16 and multiplied on
-//      v_mfma_f32_16x16x16; fp32 storage accumulates P * V on the VALU.
+//      more than 8 (so every weight stays <= 2^8); only then is the row max
+//      taken across the four lanes of a row and the sums rescaled.
+//   5. 16-bit storage: O^T += V^T P^T on v_mfma_f32_16x16x16. The weights a
+//      lane holds are exactly its P^T operand (as hi + lo halves in the
+//      storage type), so they stay in registers; V^T is read from LDS with
+//      ds_read_b64_tr_b16. fp32 storage accumulates P * V on the VALU.
 #include "attn_common.h"
 #include "fp8_encode.h"
 #include "kernels.h"
@@ -100,13 +101,17 @@ template <typename T, int D, int GT> struct Cfg {
   static constexpr bool kPvMfma = sizeof(T) == 2;
   static constexpr int kDimBlocks = D / 16;              // 16-dim output blocks (MFMA path)
   // LDS carve-up (bytes). Each wave owns one region: during the tile loop it
-  // holds the staged K tile, V tile (MFMA path) and P; afterwards the wave's
-  // partial accumulator (GT x D fp32) for the workgroup merge.
+  // holds the staged K tile and the V tile (MFMA path) or P (VALU path);
+  // afterwards the wave's partial accumulator (GT rows of D fp32) for the
+  // workgroup merge.
   static constexpr int kKstBytes = kTileTokens * kCh * 16;
   static constexpr int kVstBytes = kPvMfma ? kTileTokens * kCh * 16 : 0;
-  static constexpr int kPstBytes = kPvMfma ? 2 * 16 * 16 * 2 : kTileTokens * GT * 4;
+  static constexpr int kPstBytes = kPvMfma ? 0 : kTileTokens * GT * 4;
   static constexpr int kStageBytes = kKstBytes + kVstBytes + kPstBytes;
-  static constexpr int kWaveBytes = kStageBytes > GT * D * 4 ? kStageBytes : GT * D * 4;
+  // rows of a wave's partial accumulator are padded by 16 bytes, so the
+  // 16-byte stores of eight consecutive rows fall in distinct bank groups
+  static constexpr int kAccRow = D + 4;  // floats
+  static constexpr int kWaveBytes = kStageBytes > GT * kAccRow * 4 ? kStageBytes : GT * kAccRow * 4;
   static constexpr int kKstOff = 0;                      // within a wave region
   static constexpr int kVstOff = kKstBytes;
   static constexpr int kPstOff = kKstBytes + kVstBytes;
@@ -646,13 +651,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   }
   // tokens the item's rows may see: [tok0, ctx)
   const int ctx = MODE == kModeChunk ? L - nq + (row0 + nh - 1) / G + 1 : L;
-  // last visible token of rows 4 kg + r of this lane (chunk rows)
-  int lim[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = 4 * (lane >> 4) + r;
-    lim[r] = i < nh ? L - nq + (row0 + i) / G : -1;
-  }
+  // last visible token of this lane's row (lane % 16) (chunk rows)
+  const int lim = (lane & 15) < nh ? L - nq + (row0 + (lane & 15)) / G : -1;
   if (start >= ctx) return;
   const int end = min(ctx, start + P);
   const int nparts = (ctx - tok0 + P - 1) / P;
@@ -734,17 +734,12 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   constexpr bool kQReg = !F8 && C::kPvMfma;
   u32x4_t qreg[kQReg ? C::kSteps : 1];
 
-  // Running softmax state per head row: lanes (kg, n) own heads 4 kg + r.
-  // m[r] is a reference max in base-2 units, uniform across the 16 lanes of
-  // the row; l[r] is this lane's share (token n) of the weight sum.
-  float m[4], l[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m[r] = -INFINITY;
-    l[r] = 0.f;
-  }
+  // Running softmax state of head row n, held by the four lanes (kg, n):
+  // m is a reference max in base-2 units (the same in the four lanes), l this
+  // lane's share (tokens 4 kg .. 4 kg + 3 of each tile) of the weight sum.
+  float m = -INFINITY, l = 0.f;
 
-  // Accumulators. MFMA path: acc[b][r] = O[head 4 kg + r][dim 16 b + n].
+  // Accumulators. MFMA path (O^T): acc[b][r] = O[head n][dim 16 b + 4 kg + r].
   // VALU path: accv[h][e] = partial O[head h][dim (lane % kCh) * kEpc + e] over
   // this lane's token row.
   f32x4_t acc[C::kPvMfma ? C::kDimBlocks : 1];
@@ -756,19 +751,13 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
 #pragma unroll
     for (int e = 0; e < (C::kPvMfma ? 1 : kEpc); ++e) accv[h][e] = 0.f;
 
-  // MFMA path: this lane's byte offsets for the transposed reads. Source lane
-  // (r = (lane % 16) / 4, q = lane % 4) of group kg addresses token 4 kg + r:
-  // for P (hi/lo rows of 16 heads) heads 4q..4q+3, for V dims 16 b + 4q..4q+3.
+  // MFMA path: this lane's byte offset for the transposed V reads. Source
+  // lane (r = (lane % 16) / 4, q = lane % 4) of group kg addresses token
+  // 4 kg + r, dims 16 b + 4q .. 4q + 3.
   const int tr_tok = 4 * kg + ((lane & 15) >> 2);
   const int tr_q = lane & 3;
-  const int p_tr_off = tr_tok * 32 + tr_q * 8;
   const int v_tr_base = tr_tok * kCh * 16 + tr_q * 8;
   const int v_tr_swz = vst_swz<kCh>(tr_tok);
-  if constexpr (C::kPvMfma) {
-    // heads this workgroup does not own stay zero in the staged P
-    for (int i = lane; i < 2 * 16 * 16 / 8; i += 64)
-      reinterpret_cast<uint2 *>(pst)[i] = make_uint2(0u, 0u);
-  }
 
   // The reference max may trail the true running max by up to kLazy (base-2
   // units), so every weight p = 2^(z - m) stays <= 2^kLazy. It is raised, and
@@ -872,45 +861,44 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // S^T = K Q^T: lane (kg, n) receives tokens 4 kg + r of head row n, which
+    // is also the layout P^T takes as the B operand of O^T += V^T P^T below,
+    // so the weights never leave the registers
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < C::kSteps; ++c)
-      sc = mfma_chunk<T>(kQReg ? qreg[kQReg ? c : 0] : (n < GT ? qs[kst_slot<kCh>(n, kg + 4 * c)] : u32x4_t{0u, 0u, 0u, 0u}),
-                         kst[kst_slot<kCh>(n, kg + 4 * c)], sc);
+      sc = mfma_chunk<T>(kst[kst_slot<kCh>(n, kg + 4 * c)],
+                         kQReg ? qreg[kQReg ? c : 0] : (n < GT ? qs[kst_slot<kCh>(n, kg + 4 * c)] : u32x4_t{0u, 0u, 0u, 0u}),
+                         sc);
 
     // scores in base-2 units; tokens past the sequence (chunk rows: past the
     // row's position) get -inf
-    const bool tok_ok = n < valid;
     float z[4];
     bool over = false;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
+      const int t = 4 * kg + r;
       if constexpr (MODE == kModeChunk)
-        z[r] = tok_ok && ti * kTileTokens + n <= lim[r] ? sc[r] * sl2 : -INFINITY;
+        z[r] = t < valid && ti * kTileTokens + t <= lim ? sc[r] * sl2 : -INFINITY;
       else
-        z[r] = tok_ok ? sc[r] * sl2 : -INFINITY;
-      over |= z[r] > m[r] + kLazy;
+        z[r] = t < valid ? sc[r] * sl2 : -INFINITY;
+      over |= z[r] > m + kLazy;
     }
     if (__builtin_amdgcn_ballot_w64(over) != 0) {  // uniform: raise the reference
-      float alpha[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float mn = fmaxf(m[r], row_max16(z[r]));
-        alpha[r] = __builtin_amdgcn_exp2f(m[r] - mn);  // 0 on the first tile (m = -inf)
-        // chunk rows may have seen nothing yet (mn = -inf): keep them empty
-        if constexpr (MODE == kModeChunk) alpha[r] = mn == -INFINITY ? 1.f : alpha[r];
-        m[r] = mn;
-        l[r] *= alpha[r];
-      }
+      // row max over the tile: this lane's four tokens, then the four lanes of the row
+      const float mn = fmaxf(m, cols_max4(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]))));
+      float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first tile (m = -inf)
+      // chunk rows may have seen nothing yet (mn = -inf): keep them empty
+      if constexpr (MODE == kModeChunk) alpha = mn == -INFINITY ? 1.f : alpha;
+      m = mn;
+      l *= alpha;
       if constexpr (C::kPvMfma) {
 #pragma unroll
-        for (int b = 0; b < C::kDimBlocks; ++b)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[b][r] *= alpha[r];
+        for (int b = 0; b < C::kDimBlocks; ++b) acc[b] *= alpha;
       } else {
 #pragma unroll
         for (int h = 0; h < GT; ++h) {
-          const float ah = readlane_f(alpha[h & 3], (h >> 2) * 16);
+          const float ah = readlane_f(alpha, h);
 #pragma unroll
           for (int e = 0; e < kEpc; ++e) accv[h][e] *= ah;
         }
@@ -919,42 +907,32 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
     float p[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      p[r] = __builtin_amdgcn_exp2f(z[r] - m[r]);
+      p[r] = __builtin_amdgcn_exp2f(z[r] - m);
       if constexpr (MODE == kModeChunk) p[r] = z[r] == -INFINITY ? 0.f : p[r];  // also when m = -inf
-      l[r] += p[r];
+      l += p[r];
     }
 
     if constexpr (C::kPvMfma) {
-      // P as hi + lo in the storage type (about 16 mantissa bits together)
-      if (4 * kg < GT) {
-        typename Pv<T>::v4 hi, lo;
+      // P^T as hi + lo in the storage type (about 16 mantissa bits together);
+      // columns past the item's rows only feed output columns nobody reads
+      typename Pv<T>::v4 hi, lo;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float pr = (4 * kg + r < GT) ? p[r] : 0.f;
-          hi[r] = static_cast<T>(pr);
-          lo[r] = static_cast<T>(pr - static_cast<float>(hi[r]));
-        }
-        *reinterpret_cast<typename Pv<T>::v4 *>(pst + n * 32 + kg * 8) = hi;
-        *reinterpret_cast<typename Pv<T>::v4 *>(pst + 512 + n * 32 + kg * 8) = lo;
+      for (int r = 0; r < 4; ++r) {
+        hi[r] = static_cast<T>(p[r]);
+        lo[r] = static_cast<T>(p[r] - static_cast<float>(hi[r]));
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const typename Pv<T>::v4 pa_hi = lds_read_tr<T>(pst + p_tr_off);
-      const typename Pv<T>::v4 pa_lo = lds_read_tr<T>(pst + 512 + p_tr_off);
 #pragma unroll
       for (int b = 0; b < C::kDimBlocks; ++b) {
         const typename Pv<T>::v4 vb = lds_read_tr<T>(vst + v_tr_base + (((2 * b) ^ v_tr_swz) << 4));
-        acc[b] = Pv<T>::mfma(pa_hi, vb, acc[b]);
-        acc[b] = Pv<T>::mfma(pa_lo, vb, acc[b]);
+        acc[b] = Pv<T>::mfma(vb, hi, acc[b]);
+        acc[b] = Pv<T>::mfma(vb, lo, acc[b]);
       }
     } else {
       float *pstf = reinterpret_cast<float *>(pst);
       // p[token][head] -> LDS for the V layout
-      if (4 * kg < GT) {
+      if (n < GT) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (4 * kg + r < GT) pstf[n * GT + 4 * kg + r] = p[r];
+        for (int r = 0; r < 4; ++r) pstf[(4 * kg + r) * GT + n] = p[r];
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -1085,8 +1063,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   }
 
   // ---- wave totals to LDS
-#pragma unroll
-  for (int r = 0; r < 4; ++r) l[r] = row_sum16(l[r]);
+  l = cols_sum4(l);
   // the wave's staging area is free now: it takes the wave's partial sums
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -1095,13 +1072,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   float2 *mml = reinterpret_cast<float2 *>(smem + C::kMlOff) + wave * GT;
   int *mbad = reinterpret_cast<int *>(smem + C::kBadOff);
   if constexpr (C::kPvMfma) {
-    if (4 * kg < GT) {
+    if (n < GT) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (4 * kg + r < GT) {
-#pragma unroll
-          for (int b = 0; b < C::kDimBlocks; ++b) macc[(4 * kg + r) * D + 16 * b + n] = acc[b][r];
-        }
+      for (int b = 0; b < C::kDimBlocks; ++b)
+        *reinterpret_cast<f32x4_t *>(macc + n * C::kAccRow + 16 * b + 4 * kg) = acc[b];
     }
   } else {
     // token-row sums of the VALU accumulators
@@ -1115,14 +1089,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
 #pragma unroll
       for (int h = 0; h < GT; ++h)
 #pragma unroll
-        for (int e = 0; e < kEpc; ++e) macc[h * D + lane * kEpc + e] = accv[h][e];
+        for (int e = 0; e < kEpc; ++e) macc[h * C::kAccRow + lane * kEpc + e] = accv[h][e];
     }
   }
-  if (n == 0 && 4 * kg < GT) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (4 * kg + r < GT) mml[4 * kg + r] = make_float2(m[r], l[r]);
-  }
+  if (kg == 0 && n < GT) mml[n] = make_float2(m, l);
   if (lane == 0) mbad[wave] = bad ? 1 : 0;
   __syncthreads();
 
@@ -1159,7 +1129,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
       const float2 ml = ml_all[w * GT + h];
       const float f = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
       den = fmaf(f, ml.y, den);
-      num = fmaf(f, acc_of(w)[h * D + d], num);
+      num = fmaf(f, acc_of(w)[h * C::kAccRow + d], num);
     }
     if constexpr (F8) num *= vsc;
     if (any_bad) {
