@@ -728,6 +728,14 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   char *vst = wreg + C::kVstOff;
   char *pst = wreg + C::kPstOff;
   const u32x4_t *qs = reinterpret_cast<const u32x4_t *>(smem + C::kQOff);
+  // slot of chunk ch of token tr in the staged K tile; FP8 staging writes a
+  // lane's two chunks (2 c, 2 c + 1) in two passes, so its layout first moves
+  // the chunk's low bit to the top: the eight lanes of a token then write
+  // eight distinct bank groups in each pass
+  auto kslot = [&](int tr, int ch) {
+    if constexpr (F8) return kst_slot<kCh>(tr, (ch >> 1) | ((ch & 1) * (kCh / 2)));
+    else return kst_slot<kCh>(tr, ch);
+  };
   // 16-bit pools keep the wave's Q operand in registers for the whole item
   // (read from LDS once, after the workgroup has staged it) instead of
   // reading it from LDS for every tile
@@ -797,8 +805,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
         const int c8 = u - tr * kChKV;
         u32x4_t lo, hi;
         fp8x16_to<T>(rg.k[i], lo, hi);
-        kst[kst_slot<kCh>(tr, 2 * c8)] = lo;
-        kst[kst_slot<kCh>(tr, 2 * c8 + 1)] = hi;
+        kst[kslot(tr, 2 * c8)] = lo;
+        kst[kslot(tr, 2 * c8 + 1)] = hi;
       }
       if (has_next && kEarlyK) load_k(noff, rg);
 #pragma unroll
@@ -807,8 +815,9 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
         const int tr = u / kChKV;
         const int c8 = u - tr * kChKV;
         u32x4_t lo, hi;
-        fp8x16_to<T>(rg.v[i], lo, hi);
-        if (partial && tr >= valid) lo = hi = u32x4_t{0u, 0u, 0u, 0u};
+        // rows past the sequence: code 0 is +0 (four selects here instead of
+        // eight on the decoded chunks)
+        fp8x16_to<T>(partial && tr >= valid ? u32x4_t{0u, 0u, 0u, 0u} : rg.v[i], lo, hi);
         vs[tr * kCh + ((2 * c8) ^ vst_swz<kCh>(tr))] = lo;
         vs[tr * kCh + ((2 * c8 + 1) ^ vst_swz<kCh>(tr))] = hi;
       }
@@ -853,7 +862,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
       if (holds_new && ti == tok_new / kTileTokens) {  // uniform
         const int tr = tok_new % kTileTokens;
         const u32x4_t *nr = reinterpret_cast<const u32x4_t *>(smem + C::kNewOff);
-        if (lane < kCh) kst[kst_slot<kCh>(tr, lane)] = nr[lane];
+        if (lane < kCh) kst[kslot(tr, lane)] = nr[lane];
         else if (lane < 2 * kCh)
           reinterpret_cast<u32x4_t *>(vst)[tr * kCh + ((lane - kCh) ^ vst_swz<kCh>(tr))] = nr[lane];
       }
@@ -867,7 +876,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < C::kSteps; ++c)
-      sc = mfma_chunk<T>(kst[kst_slot<kCh>(n, kg + 4 * c)],
+      sc = mfma_chunk<T>(kst[kslot(n, kg + 4 * c)],
                          kQReg ? qreg[kQReg ? c : 0] : (n < GT ? qs[kst_slot<kCh>(n, kg + 4 * c)] : u32x4_t{0u, 0u, 0u, 0u}),
                          sc);
 
