@@ -49,7 +49,12 @@ def measured_traffic(cfg, fused=True, fp8=False):
     committed FETCH_SIZE/WRITE_SIZE summary of that step under profiles/, not
     measured in this run; (None, reason) when there is none or the decode
     source changed since the counters were taken."""
-    name = PROFILE_NAMES[cfg] + ("_fp8" if fp8 else "") + ("" if fused else "_two_call")
+    return committed_traffic(PROFILE_NAMES[cfg] + ("_fp8" if fp8 else "") + ("" if fused else "_two_call"))
+
+
+def committed_traffic(name):
+    """(HBM bytes per call, source) from profiles/<name>_traffic.json, or
+    (None, reason) when there is none or the decode source changed since."""
     rel = os.path.join("profiles", name + "_traffic.json")
     try:
         with open(os.path.join(ROOT, rel)) as f:
@@ -299,6 +304,12 @@ def bench_shared_prefix(args, dev):
         us = e0.elapsed_time(e1) * 1e3 / args.steps
         res[name] = {"us": round(us, 3), "GBps_compulsory": round(comp / (us * 1e-6) / 1e9, 1)}
     sp = res["shared_prefix"]
+    traffic, traffic_src = committed_traffic("paged_shared_prefix_prompt_samples_f16")
+    extra = {}
+    if not args.no_ceiling:
+        # also the 2 GiB device copy that scales FETCH_SIZE / WRITE_SIZE in
+        # the counter summaries of this op
+        extra["stream_ceiling_gbs"] = stream_ceiling(dev)
     print(json.dumps({
         "metric": "shared-prefix decode: compulsory-byte HBM GB/s", "value": sp["GBps_compulsory"], "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "dtype": "f16",
@@ -306,9 +317,11 @@ def bench_shared_prefix(args, dev):
         "config": {"workload": workloads.CONFIG_NAMES[5], "groups": int(len(gs) - 1), "max_group_size": int(mg),
                    "compulsory_bytes": comp, "logical_bytes": logical, **res},
         "roofline": {"bound": "hbm", "achieved": sp["GBps_compulsory"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(sp["GBps_compulsory"] / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "paged_attn_decode_shared_prefix call (prefix + suffix kernels)",
+                     "frac": round(sp["GBps_compulsory"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "traffic_source": traffic_src,
+                     "kernel": "paged_attn_decode_shared_prefix call (decode kernel, shared mode, one launch)",
                      "algorithmic_bytes": comp},
+        **extra,
     }), flush=True)
 
 

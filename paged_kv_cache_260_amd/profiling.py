@@ -130,7 +130,7 @@ def read_trace(path):
 
 
 def summarize(name, command, stats_csv, fetch_csv, write_csv, algorithmic_bytes, copy_bytes, out,
-              fetch_command=None, write_command=None, trace_csv=None, skip=0, take=0):
+              fetch_command=None, write_command=None, trace_csv=None, skip=0, take=0, only=None):
     os.makedirs(out, exist_ok=True)
     stats = read_stats(stats_csv)
     lines = [f"# {name}: rocprofv3 kernel statistics", "", "Command (repository root):", "",
@@ -182,6 +182,8 @@ def summarize(name, command, stats_csv, fetch_csv, write_csv, algorithmic_bytes,
         for k in sorted(fetch):
             if not any(k == c or k.startswith(c + " (") for c in CALL_KERNELS):
                 continue
+            if only and k not in only:  # a run that times several kinds of call
+                continue
             per_kernel[k] = {"fetch_kib_raw": avg(fetch, k), "write_kib_raw": avg(write, k),
                              "fetch_bytes": avg(fetch, k) * f_scale * 1024,
                              "write_bytes": avg(write, k) * w_scale * 1024}
@@ -208,8 +210,8 @@ def summarize(name, command, stats_csv, fetch_csv, write_csv, algorithmic_bytes,
               f"Decode source hash: `{result['decode_source_hash']}`."]
         with open(os.path.join(out, f"{name}_traffic.md"), "w") as f:
             f.write("\n".join(t) + "\n")
-    with open(os.path.join(out, f"{name}_traffic.json"), "w") as f:
-        json.dump(result, f, indent=1)
+        with open(os.path.join(out, f"{name}_traffic.json"), "w") as f:
+            json.dump(result, f, indent=1)
     return result
 
 
@@ -327,9 +329,11 @@ def main():
     ap.add_argument("--trace", help="kernel trace CSV of the statistics run")
     ap.add_argument("--skip", type=int, default=0, help="untimed calls before the timed ones")
     ap.add_argument("--take", type=int, default=0, help="timed calls")
+    ap.add_argument("--only", action="append",
+                    help="count only this kernel label in the call's traffic (repeatable)")
     a = ap.parse_args()
     r = summarize(a.name, a.command, a.stats, a.fetch, a.write, a.algorithmic_bytes, a.copy_bytes,
-                  a.out, a.fetch_command, a.write_command, a.trace, a.skip, a.take)
+                  a.out, a.fetch_command, a.write_command, a.trace, a.skip, a.take, a.only)
     print(json.dumps(r))
 
 
