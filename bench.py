@@ -249,17 +249,20 @@ def bench_chunk(args, dev):
         del kps, vps
         torch.cuda.empty_cache()
     sv, pf = results["spec_verify_qlen4"], results["prefill_chunk512"]
+    traffic, traffic_src = committed_traffic("paged_decode_chunk_rows_spec_verify_b128")
+    extra = {} if args.no_ceiling else {"stream_ceiling_gbs": stream_ceiling(dev)}
     print(json.dumps({
         "metric": "chunk attention: effective HBM GB/s (speculative verify) and TFLOP/s (prefill chunk)",
         "value": sv["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "paged chunk attention, causal inside the chunk", **results},
         "roofline": {"bound": "hbm", "achieved": sv["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(sv["GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "paged_chunk_kernel (speculative verify)", "algorithmic_bytes": sv["bytes"]},
+                     "frac": round(sv["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic, "traffic_source": traffic_src,
+                     "kernel": "paged_decode_kernel, chunk rows (speculative verify)", "algorithmic_bytes": sv["bytes"]},
         "roofline_prefill": {"bound": "mfma", "achieved": pf["TFLOPs"], "peak": 2500.0, "unit": "TFLOP/s",
                              "frac": round(pf["TFLOPs"] / 2500.0, 4), "kernel": "paged_chunk_kernel (prefill chunk)",
                              "algorithmic_flops": pf["flops"]},
+        **extra,
     }), flush=True)
 
 
