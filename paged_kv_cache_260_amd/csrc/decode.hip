@@ -122,7 +122,8 @@ template <typename T, int D, int GT> struct Cfg {
   // slot totals, [32, 48) own slot base
   static constexpr int kMemOff = kFlagOff + 4;
   // Q of the item (its GT head rows, swizzled like a K tile), shared by the
-  // four waves as the MFMA A operand; rows GT..15 of the operand are zero
+  // four waves as the MFMA B operand of S^T = K Q^T; rows GT..15 of the
+  // operand are zero
   static constexpr int kQOff = (kMemOff + 48 * 4 + 15) / 16 * 16;
   static constexpr int kQChunks = GT * kCh;
   static constexpr int kQPer = (kQChunks + kNW * 64 - 1) / (kNW * 64);  // Q chunks per thread
