@@ -36,6 +36,7 @@ from paged_kv_cache_260_amd import _lib, accounting, profiling, workloads  # noq
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 FUSED_MERGE_PARTS = 8          # partition counts merged inside the decode kernel
 MALL_BYTES = 256 * 2 ** 20     # memory-side (Infinity) cache
+HOLD_CYCLES = 250_000          # GPU spin before the timed region (~0.1 ms)
 METRIC = "paged decode effective HBM GB/s (% of MI355X peak) + us/batch, GQA bs=128"
 DTYPE_NAMES = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
 # profile summaries under profiles/, by workload
@@ -465,6 +466,12 @@ def main():
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"[bench] timing {K} steps")
     torch.cuda.synchronize()
+    # An untimed hold on the GPU (a spin of about 0.1 ms) before the start
+    # event: the host then has the first timed steps queued by the time the
+    # event runs, so the figure covers the K steps and not the host's latency
+    # to submit the first one (about 10 us through the binding, 0.5 us per
+    # step when K is 20).
+    torch.cuda._sleep(HOLD_CYCLES)
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(K):
