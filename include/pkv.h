@@ -173,6 +173,34 @@ PKV_API int pkv_paged_attn_decode_append(void *out, const void *q, void *k_pool,
                                          int64_t num_blocks, int32_t dtype, void *stream);
 
 /*
+ * pkv_paged_attn_decode_append with the lengths also given in host memory.
+ * The vLLM notes page's engine step has the scheduler, on the host, decide
+ * each step's batch and lengths before the forward pass runs; a caller that
+ * holds them there passes them here, and the library builds the work order
+ * (which workgroup takes which sequence partition, longest first) on the host
+ * and hands it to the kernel with the launch. The workgroups then start their
+ * first items at once instead of first loading every length and building
+ * that order themselves.
+ *
+ * Arguments: as in pkv_paged_attn_decode_append, plus
+ *   seq_lens_host   host memory, [num_seqs] int32, the values seq_lens holds
+ *                   on the device; read during the call only, owned by the
+ *                   caller (PKV_ERR_INVALID if null while num_seqs > 0)
+ * Results are those of pkv_paged_attn_decode_append, bit for bit. The order
+ * is used when the batch has at most 256 sequences and every workgroup takes
+ * one item; other batches take the kernel's own order. A sequence whose
+ * device length splits into a different number of partitions than its host
+ * length gets NaN rows and its new token is not stored (one with the same
+ * count is attended over its device length); other sequences are unaffected.
+ */
+PKV_API int pkv_paged_attn_decode_append_planned(void *out, const void *q, void *k_pool, void *v_pool,
+                                                 const void *k_new, const void *v_new, const int32_t *block_tables,
+                                                 const int32_t *seq_lens, const int32_t *seq_lens_host, float scale,
+                                                 int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                                                 int32_t block_size, int32_t num_seqs, int32_t max_blocks_per_seq,
+                                                 int64_t num_blocks, int32_t dtype, void *stream);
+
+/*
  * pkv_paged_attn_decode for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc. Same arguments, result, checks and kernels as

@@ -248,7 +248,7 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
                 int32_t n_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_seqs,
                 int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype, void *stream, bool fp8,
                 const float *k_scale, const float *v_scale, const void *k_new = nullptr,
-                const void *v_new = nullptr, bool no_alloc = false) {
+                const void *v_new = nullptr, bool no_alloc = false, const int32_t *host_seq_lens = nullptr) {
   if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID, "unknown dtype %d", dtype);
   if (fp8 && dtype == PKV_F32)
     return fail(PKV_ERR_UNSUPPORTED, "FP8 pools need a float16 or bfloat16 query and output");
@@ -307,6 +307,7 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
   a.v_scale = v_scale;
   a.k_new = k_new;
   a.v_new = v_new;
+  a.host_seq_lens = host_seq_lens;
   plan(block_size, max_blocks_per_seq, &a.partition_tokens, &a.max_parts);
   if ((int64_t)num_seqs * a.max_parts * n_kv_heads * a.head_chunks > (int64_t)INT32_MAX)
     return fail(PKV_ERR_INVALID, "%d sequences x %d partitions x %d heads: too many workgroups",
@@ -390,6 +391,18 @@ int pkv_paged_attn_decode_append(void *out, const void *q, void *k_pool, void *v
   return decode_impl(out, q, k_pool, v_pool, block_tables, seq_lens, scale, n_heads, n_kv_heads, head_dim,
                      block_size, num_seqs, max_blocks_per_seq, num_blocks, dtype, stream, false, nullptr, nullptr,
                      k_new, v_new);
+}
+
+int pkv_paged_attn_decode_append_planned(void *out, const void *q, void *k_pool, void *v_pool, const void *k_new,
+                                         const void *v_new, const int32_t *block_tables, const int32_t *seq_lens,
+                                         const int32_t *seq_lens_host, float scale, int32_t n_heads,
+                                         int32_t n_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_seqs,
+                                         int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
+                                         void *stream) {
+  if (num_seqs > 0 && !seq_lens_host) return fail(PKV_ERR_INVALID, "null seq_lens_host");
+  return decode_impl(out, q, k_pool, v_pool, block_tables, seq_lens, scale, n_heads, n_kv_heads, head_dim,
+                     block_size, num_seqs, max_blocks_per_seq, num_blocks, dtype, stream, false, nullptr, nullptr,
+                     k_new, v_new, false, seq_lens_host);
 }
 
 int pkv_paged_attn_decode_append_fp8(void *out, const void *q, void *k_pool, void *v_pool, const void *k_new,

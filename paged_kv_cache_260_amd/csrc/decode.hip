@@ -55,6 +55,7 @@ using namespace attn;
 // Batches of up to kCompactSeqs sequences (entities) take the longest-first
 // item order below, built per workgroup in LDS.
 constexpr int kCompactSeqs = 256;
+static_assert(kHostPlanSeqs == kCompactSeqs, "a host-built order covers the batches a compact plan does");
 constexpr int kCompactChunks = kCompactSeqs / 64;
 constexpr int kRemBuckets = 8;
 
@@ -451,7 +452,7 @@ __device__ __forceinline__ void load_item_head(const DecodeArgs &a, int tid, int
   h.ready = true;
 }
 
-template <typename T, int D, int GT, bool F8, int MODE>
+template <typename T, int D, int GT, bool F8, int MODE, bool HP = false>
 __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int tid, int unit, int s, int part,
                                             int p_pre, bool bad_desc, ItemHead<Cfg<T, D, GT>::kQPer> &hd,
                                             int s_next, int part_next) {
@@ -600,6 +601,12 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, char *smem, int
   const int64_t cap = (int64_t)a.max_blocks * a.block_size;
   bool bad_len = L < 0 || (int64_t)L > cap;
   if constexpr (MODE == kModeChunk) bad_len |= L < nq || q0 < 0;
+  if constexpr (HP) {
+    // host-built order: the device length must give the partition count the
+    // host planned for, or some partition has no item (or one too many): the
+    // sequence then takes the invalid-length path in every item
+    bad_len |= (!bad_len && L > 0 ? (L + P - 1) / P : 1) != (int)a.hp_np[s];
+  }
   if constexpr (MODE == kModePrefix) bad_len |= (L & (a.block_size - 1)) != 0;
   if constexpr (MODE == kModeSuffix) bad_len |= tok0 < 0 || tok0 > L || (tok0 & (a.block_size - 1)) != 0;
   if constexpr (SH) {
@@ -1303,7 +1310,7 @@ template <typename T, int D, int GT, bool F8> constexpr int decode_waves_per_eu(
   return F8 ? 4 : (sizeof(T) == 2 || GT <= 4) ? 3 : 2;
 }
 
-template <typename T, int D, int GT, bool F8, int MODE>
+template <typename T, int D, int GT, bool F8, int MODE, bool HP = false>
 __global__ __launch_bounds__(kDecodeWaves * 64)
 __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT, F8>()))) void paged_decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[Cfg<T, D, GT>::kSmem];
@@ -1339,7 +1346,28 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT, F8>()))) void p
   plan.full_items = plan.items = 0;
   plan.bad_desc = false;
   int *plan_lds = reinterpret_cast<int *>(smem + Cfg<T, D, GT>::kPlanOff);
-  if (compact) make_plan<MODE>(a, plan, plan_lds, claim, ticket);
+  // HP: the work order comes built from the host (one item per workgroup)
+  // and replaces the plan, so no workgroup waits on the lengths before its
+  // first item's loads; claimers still share their ticket.
+  if constexpr (HP) {
+    plan.items = a.hp_items;
+    if (claim) {
+      if (threadIdx.x == 0) plan_lds[kPlanTicket] = (int)ticket;
+      __syncthreads();
+    }
+  } else {
+    if (compact) make_plan<MODE>(a, plan, plan_lds, claim, ticket);
+  }
+  // item j (< plan.items) -> (sequence, partition)
+  auto locate = [&](int j, int &s_out, int &p_out) {
+    if constexpr (HP) {
+      const int e = a.hp[j];
+      s_out = e & 255;
+      p_out = e >> 8;
+    } else {
+      locate_item(plan, plan_lds, a.num_seqs, j, s_out, p_out);
+    }
+  };
   // Tickets place items only when every workgroup takes one item (a unit has
   // no more items than workgroups); with two or more rounds per workgroup the
   // fixed places measured faster. Every claimer has drawn its ticket either
@@ -1364,7 +1392,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT, F8>()))) void p
   int s = -1, part = 0;
   if (compact) {
     const int64_t j = item_of(0);
-    if (j >= 0) locate_item(plan, plan_lds, a.num_seqs, (int)j, s, part);
+    if (j >= 0) locate((int)j, s, part);
   } else {
     part = w / a.num_seqs;
     s = (w % a.num_seqs + a.num_seqs - part % a.num_seqs) % a.num_seqs;
@@ -1373,7 +1401,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT, F8>()))) void p
     int s_next = -1, part_next = 0;
     if (compact) {
       const int64_t jn = item_of(round + 1);
-      if (jn >= 0) locate_item(plan, plan_lds, a.num_seqs, (int)jn, s_next, part_next);
+      if (jn >= 0) locate((int)jn, s_next, part_next);
     }
     s = __builtin_amdgcn_readfirstlane(s);
     part = __builtin_amdgcn_readfirstlane(part);
@@ -1388,7 +1416,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT, F8>()))) void p
     // prefix partition length (shared mode): the plan's, or the host's minimum
     // shared mode: a description is checked only by the longest-first plan,
     // which the host always picks for one-launch shared calls
-    decode_item<T, D, GT, F8, MODE>(a, smem, tid, unit, s, part, compact ? plan.p_pre : a.prefix_partition_tokens,
+    decode_item<T, D, GT, F8, MODE, HP>(a, smem, tid, unit, s, part, compact ? plan.p_pre : a.prefix_partition_tokens,
                                     !compact || plan.bad_desc, hd, s_next, part_next);
     s = s_next;
     part = part_next;
@@ -1645,6 +1673,38 @@ namespace {
 // never more than the unit's largest possible item count.
 constexpr int kWgsPerSlot = 2;
 
+// The longest-first order of make_plan, built on the host from the host
+// copy of the lengths, for launches whose workgroups take one item each
+// (tickets on, no more items per unit than workgroups). Leaves hp_items at
+// zero, and the kernel on its own plan, when the order does not fit the
+// arguments.
+void host_plan(DecodeArgs &a) {
+  const int B = a.num_seqs;
+  const int P = a.partition_tokens;
+  const int64_t max_tok = (int64_t)a.max_blocks * a.block_size;
+  if (B > kHostPlanSeqs || P < 1) return;
+  int full[kHostPlanSeqs], bucket[kHostPlanSeqs];
+  int64_t items = B;
+  for (int s = 0; s < B; ++s) {
+    const int L = a.host_seq_lens[s];
+    const bool ok = L > 0 && (int64_t)L <= max_tok;
+    full[s] = ok ? (L - 1) / P : 0;
+    if (full[s] + 1 > 255) return;  // partition ids take 8 bits
+    bucket[s] = ok ? (int)((int64_t)(P - (L - full[s] * P)) * kRemBuckets / P) : kRemBuckets;
+    items += full[s];
+  }
+  if (items > kHostPlanItems || items > a.wgs_per_unit) return;
+  int n = 0;
+  for (int s = 0; s < B; ++s) {
+    for (int p = 0; p < full[s]; ++p) a.hp[n++] = (uint16_t)(s | (p << 8));
+    a.hp_np[s] = (uint8_t)(full[s] + 1);
+  }
+  for (int b = 0; b <= kRemBuckets; ++b)
+    for (int s = 0; s < B; ++s)
+      if (bucket[s] == b) a.hp[n++] = (uint16_t)(s | (full[s] << 8));
+  a.hp_items = n;
+}
+
 template <typename T, int D, int GT, bool F8, int MODE = kModeDecode>
 hipError_t launch_t(const DecodeArgs &args, hipStream_t stream) {
   DecodeArgs a = args;
@@ -1680,8 +1740,20 @@ hipError_t launch_t(const DecodeArgs &args, hipStream_t stream) {
     a.wgs_per_unit = (int32_t)max_items;
     a.tickets = nullptr;
   }
+  a.hp_items = 0;
+  if constexpr (MODE == kModeAppend && !F8) {
+    if (a.host_seq_lens && a.tickets) host_plan(a);
+  }
   dim3 grid((unsigned)(units * a.wgs_per_unit), 1, 1);
-  hipLaunchKernelGGL((paged_decode_kernel<T, D, GT, F8, MODE>), grid, dim3(kDecodeWaves * 64), 0, stream, a);
+  if constexpr (MODE == kModeAppend && !F8) {
+    if (a.hp_items > 0)
+      hipLaunchKernelGGL((paged_decode_kernel<T, D, GT, F8, MODE, true>), grid, dim3(kDecodeWaves * 64), 0, stream,
+                         a);
+    else
+      hipLaunchKernelGGL((paged_decode_kernel<T, D, GT, F8, MODE>), grid, dim3(kDecodeWaves * 64), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((paged_decode_kernel<T, D, GT, F8, MODE>), grid, dim3(kDecodeWaves * 64), 0, stream, a);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.max_parts == 1 || a.arrivals != nullptr) return err;
   if constexpr (MODE == kModeChunk || MODE == kModePrefix) {

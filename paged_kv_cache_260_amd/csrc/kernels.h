@@ -18,6 +18,11 @@ constexpr int kDecodeWaves = 4;
 // lane in a single VGPR.
 constexpr int kMaxPartitionBlocks = 64;
 
+// Host-built work order (pkv_paged_attn_decode_append_planned): at most this
+// many items per unit, for batches of at most kHostPlanSeqs sequences.
+constexpr int kHostPlanItems = 1024;
+constexpr int kHostPlanSeqs = 256;
+
 struct DecodeArgs {
   void *out;
   const void *q;
@@ -81,6 +86,16 @@ struct DecodeArgs {
   // encoded with k_scale / v_scale on their way in)
   const void *k_new;
   const void *v_new;
+  // Host memory, read by the launch only (null: none): the lengths seq_lens
+  // holds on the device, from which the launch may build the work order.
+  const int32_t *host_seq_lens;
+  // Work order built on the host (hp_items > 0): item j of a unit is sequence
+  // hp[j] & 255, partition hp[j] >> 8, and the workgroups skip the
+  // longest-first plan; hp_np[s] is the partition count the host derived
+  // for sequence s, which every item of s checks against the device length.
+  int32_t hp_items;
+  uint16_t hp[kHostPlanItems];
+  uint8_t hp_np[kHostPlanSeqs];
 };
 
 // Largest partition count merged inside the decode kernel; longer tables use

@@ -28,6 +28,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -91,9 +92,11 @@ def short_name(name: str) -> str:
                 "kv_cache_write_kernel",
                 "zero_i32_kernel", "copy_blocks_kernel", "stream_read_kernel", "gather_tiles_kernel", COPY_KERNEL):
         if key in name:
-            if key == DECODE_KERNEL and name.endswith("EEEvNS_10DecodeArgsE") and "ELi" in name:
-                mode = name[: -len("EEEvNS_10DecodeArgsE")].rsplit("ELi", 1)[-1]
-                return key + _DECODE_MODES.get(mode, "")
+            # the mode, then (when present) whether the work order came from the host
+            m = re.search(r"ELi(\d)(?:ELb([01]))?EEEvNS_10DecodeArgsE$", name) if key == DECODE_KERNEL else None
+            if m:
+                label = key + _DECODE_MODES.get(m.group(1), "")
+                return label[:-1] + ", host order)" if m.group(2) == "1" and label.endswith(")") else label
             return key
     return name[:60]
 

@@ -76,6 +76,30 @@ def test_decode_rejects_bad_arguments(over, status):
     assert _lib.last_error() != ""
 
 
+def _planned(**over):
+    args = dict(out=16, q=16, k_pool=16, v_pool=16, k_new=16, v_new=16, block_tables=16, seq_lens=16,
+                seq_lens_host=16, scale=0.125, n_heads=32, n_kv_heads=8, head_dim=128, block_size=16, num_seqs=4,
+                max_blocks_per_seq=8, num_blocks=64, dtype=2, stream=None)
+    args.update(over)
+    return _lib.lib().pkv_paged_attn_decode_append_planned(*args.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(seq_lens_host=None), _lib.PKV_ERR_INVALID),     # the host copy of the lengths is required
+    (dict(dtype=0), _lib.PKV_ERR_UNSUPPORTED),            # float32: the one-call step is 16-bit only
+    (dict(k_new=None), _lib.PKV_ERR_INVALID),
+    (dict(n_heads=30), _lib.PKV_ERR_INVALID),
+    (dict(v_pool=24), _lib.PKV_ERR_INVALID),              # misaligned
+])
+def test_planned_append_rejects_bad_arguments(over, status):
+    assert _planned(**over) == status
+    assert _lib.last_error() != ""
+
+
+def test_planned_append_empty_batch_is_noop():
+    assert _planned(num_seqs=0, seq_lens_host=None, q=None, out=None) == _lib.PKV_OK
+
+
 def test_decode_empty_batch_is_noop():
     assert _decode(num_seqs=0, q=None, out=None) == _lib.PKV_OK
     assert _lib.last_error() == ""

@@ -36,7 +36,9 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_append(w, lens):
+def run_append(w, lens, host_lens=None):
+    """The one-call step; with host_lens, the planned call (the lengths also
+    in host memory, the work order built from them)."""
     dev = "cuda"
     kp, vp = w.k_pool.to(dev), w.v_pool.to(dev)
     q = w.q.to(dev)
@@ -44,9 +46,14 @@ def run_append(w, lens):
     _lib.paged_attn_decode_append(out, q, kp, vp, w.k_new.to(dev), w.v_new.to(dev),
                                   torch.from_numpy(w.block_tables).to(dev),
                                   torch.from_numpy(np.asarray(lens, np.int32)).to(dev), w.scale, w.n_heads,
-                                  w.n_kv_heads, w.head_dim, w.block_size)
+                                  w.n_kv_heads, w.head_dim, w.block_size,
+                                  seq_lens_host=None if host_lens is None else np.asarray(host_lens, np.int32))
     torch.cuda.synchronize()
     return out, kp, vp
+
+
+def same_bits(a, b):
+    return torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
 def run_two_calls(w, lens):
@@ -159,3 +166,80 @@ def test_ticket_placement_repeats_across_grids():
     err = max_abs_err(outs[2], oracle_step(ws[0], lens))
     say(f"  third call max abs err {err:.3e}")
     assert err <= TOL[ws[0].dtype]
+
+
+# --- the planned call (work order built on the host) --------------------------
+
+@pytest.mark.parametrize("cfg", [2, 3, 5])
+def test_planned_append_equals_append(cfg):
+    """The planned call gives the one-call step's bits (output and pools) on
+    the MHA, GQA and shared-prompt workloads; the MHA batch, whose workgroups
+    take two or more items, keeps the kernel's own order."""
+    say(f"planned append cfg{cfg}")
+    w = workloads.make(cfg, poison=True)
+    lens = w.seq_lens_after_write()
+    out, kp, vp = run_append(w, lens)
+    out2, kp2, vp2 = run_append(w, lens, host_lens=lens)
+    assert same_bits(out, out2) and same_bits(kp, kp2) and same_bits(vp, vp2)
+    if cfg == 3:
+        err = max_abs_err(out2, oracle_step(w, lens))
+        say(f"  max abs err {err:.3e}")
+        assert err <= TOL[w.dtype]
+
+
+def test_planned_append_across_grids():
+    """Planned calls with three different grids in a row (batch 128, 40, 128;
+    the host order with ticket claimers, then the kernel's own plan for the
+    small batch), each bit-identical to the one-call step, the last also
+    against the oracle."""
+    ws = [workloads.random_case(700 + b, num_seqs=b, n_heads=32, n_kv_heads=8, head_dim=128, block_size=16,
+                                dtype=torch.bfloat16, max_len=1500, min_len=16, poison=True) for b in (128, 40)]
+    for w in (ws[0], ws[1], ws[0]):
+        say(f"planned: batch {w.num_seqs}")
+        lens = w.seq_lens_after_write()
+        out, _, _ = run_append(w, lens)
+        out2, _, _ = run_append(w, lens, host_lens=lens)
+        assert same_bits(out, out2)
+    err = max_abs_err(out2, oracle_step(ws[0], ws[0].seq_lens_after_write()))
+    say(f"  last call max abs err {err:.3e}")
+    assert err <= TOL[ws[0].dtype]
+
+
+def test_planned_append_host_length_mismatch():
+    """Host lengths that split into another partition count than the device
+    lengths give NaN rows and no write for those sequences; one with the same
+    count is attended over its device length; every other row keeps its bits,
+    and later calls on the stream (planned and not) are unaffected."""
+    w = workloads.random_case(7100, num_seqs=128, n_heads=32, n_kv_heads=8, head_dim=128, block_size=16,
+                              dtype=torch.bfloat16, max_len=1500, min_len=16, poison=True)
+    lens = w.seq_lens_after_write()
+    cap = w.block_tables.shape[1] * w.block_size
+    P, _ = _lib.decode_plan(w.n_heads, w.n_kv_heads, w.block_size, w.num_seqs, w.block_tables.shape[1])
+    long_ = [int(s) for s in np.flatnonzero(lens > P)]
+    # short[0] gets a host length one partition longer, still inside the table
+    short = [int(s) for s in np.flatnonzero((lens > 64) & (lens <= P) & (lens + P <= cap))]
+    assert len(long_) >= 2 and len(short) >= 3
+    host = lens.copy()
+    bad = [long_[0], short[0]]
+    host[long_[0]] = P            # two partitions on the device, one on the host
+    host[short[0]] = lens[short[0]] + P   # one on the device, two on the host
+    host[short[1]] = lens[short[1]] - 32  # same count: attended over the device length
+    host[short[2]] = 0                    # empty on the host, one partition either way
+    say(f"mismatch: NaN rows for {bad}")
+    ref, kref, vref = run_append(w, lens)
+    out, kp, vp = run_append(w, lens, host_lens=host)
+    o = out.float().cpu().numpy()
+    good = [s for s in range(w.num_seqs) if s not in bad]
+    assert np.isnan(o[bad]).all()
+    assert same_bits(out[good], ref[good])
+    for s in bad:  # no write: the slot keeps what it held before the call
+        blk, off = divmod(int(w.slot_mapping[s]), w.block_size)
+        assert same_bits(kp[blk, :, off].cpu(), w.k_pool[blk, :, off])
+        assert same_bits(vp[blk, :, off].cpu(), w.v_pool[blk, :, off])
+    for s in good:
+        blk, off = divmod(int(w.slot_mapping[s]), w.block_size)
+        assert same_bits(kp[blk, :, off], kref[blk, :, off])
+    # the merge counters were left clean: both kinds of call give the bits again
+    out3, _, _ = run_append(w, lens, host_lens=lens)
+    out4, _, _ = run_append(w, lens)
+    assert same_bits(out3, ref) and same_bits(out4, ref)

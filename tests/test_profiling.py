@@ -86,3 +86,11 @@ def test_no_traffic_file_without_counters(tmp_path):
     profiling.summarize("s", "cmd", str(stats), None, None, 0, 2 * 2 ** 30, str(out))
     assert (out / "s_kernel_stats.md").exists()
     assert not (out / "s_traffic.json").exists()
+
+
+def test_decode_kernel_labels_carry_mode_and_host_order():
+    base = "_ZN3pkv12_GLOBAL__N_119paged_decode_kernelIDF16bLi128ELi4ELb0ELi5"
+    assert profiling.short_name(base + "EEEvNS_10DecodeArgsE") == "paged_decode_kernel (append)"
+    assert profiling.short_name(base + "ELb0EEEvNS_10DecodeArgsE") == "paged_decode_kernel (append)"
+    assert profiling.short_name(base + "ELb1EEEvNS_10DecodeArgsE") == "paged_decode_kernel (append, host order)"
+    assert profiling.short_name(_PLAIN) == "paged_decode_kernel"
