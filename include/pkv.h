@@ -18,8 +18,10 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - All array arguments are DEVICE pointers on the current HIP device, dense
- *   and row-major, 16-byte aligned. The caller owns every array; the library
- *   keeps no pointer after a call returns.
+ *   and row-major, 16-byte aligned, except the one host array a function
+ *   names as such (seq_lens_host of pkv_paged_attn_decode_append_planned).
+ *   The caller owns every array; the library keeps no pointer after a call
+ *   returns.
  * - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means the
  *   null stream). The caller keeps the arrays alive until the stream reaches
  *   that point. Nothing synchronises the host.
