@@ -87,7 +87,9 @@ static_assert(kCompactSeqs <= 256, "remainder ranks take 8 bits of a plan entry"
 // and few enough partitions in all that the packed prefixes fit (partitions
 // are at least 16 tokens, so the batch has fewer than 2^23 of them).
 __host__ __device__ __forceinline__ bool compact_plan(const DecodeArgs &a) {
-  return a.num_seqs <= kCompactSeqs && (int64_t)a.num_seqs * a.max_blocks * a.block_size < (int64_t(1) << 27);
+  // both terms evaluated (no short circuit): a workgroup then loads the three
+  // sizes in one round trip instead of two
+  return (a.num_seqs <= kCompactSeqs) & ((int64_t)a.num_seqs * a.max_blocks * a.block_size < (int64_t(1) << 27));
 }
 
 template <typename T, int D, int GT> struct Cfg {
@@ -1328,7 +1330,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, D, GT, F8>()))) void p
   // of a long sequence spread over the chip.
   __builtin_amdgcn_s_setprio(2);
   const int units = a.n_kv_heads * a.head_chunks;
-  const bool compact = compact_plan(a);
+  const bool compact = HP || compact_plan(a);  // a host-built order implies a compact plan
   // A workgroup past the first static_wgs takes the place of workgroup
   // static_wgs + ticket_place(ticket): the claimers together cover exactly
   // those places, in the order their slots free up on any XCD, whatever value
