@@ -350,7 +350,7 @@ def main():
                     help="decode step: one call that appends the new token and decodes (default), or the "
                          "cache write followed by the decode call")
     ap.add_argument("--device-plan", action="store_true",
-                    help="16-bit one-call step: pkv_paged_attn_decode_append (the kernel builds the work order "
+                    help="one-call step: pkv_paged_attn_decode_append[_fp8] (the kernel builds the work order "
                          "from the device lengths) instead of the planned call, which also takes the lengths in "
                          "host memory and builds the order on the host every call")
     ap.add_argument("--kv", default="native", choices=["native", "fp8"],
@@ -419,10 +419,10 @@ def main():
     # step); --step two-call (and FP8 pools) time the write kernel, then decode
     # (the one-call step is built for 16-bit queries; fp32 always takes two calls)
     fused = args.step == "append" and w.dtype != torch.float32
-    # the planned call (16-bit one-call step): the lengths also go in host
+    # the planned call (one-call step): the lengths also go in host
     # memory, as a serving loop's scheduler holds them, and the library builds
     # the work order from them on the host at every call (inside the timed steps)
-    planned = fused and not fp8 and not args.device_plan
+    planned = fused and not args.device_plan
     lens_host = np.ascontiguousarray(lens1, dtype=np.int32) if planned else None
 
     def step(r, ev=None):
@@ -431,7 +431,8 @@ def main():
                 ev[0].record(stream)
             if fp8:
                 _lib.paged_attn_decode_append_fp8(out, q, kps[r], vps[r], kn, vn, ksd, vsd, bt, sl, w.scale,
-                                                  w.n_heads, w.n_kv_heads, w.head_dim, w.block_size, stream=stream)
+                                                  w.n_heads, w.n_kv_heads, w.head_dim, w.block_size, stream=stream,
+                                                  seq_lens_host=lens_host)
             else:
                 _lib.paged_attn_decode_append(out, q, kps[r], vps[r], kn, vn, bt, sl, w.scale, w.n_heads,
                                               w.n_kv_heads, w.head_dim, w.block_size, stream=stream,
@@ -569,7 +570,7 @@ def main():
             "cached_tokens": int(lens1.sum()), "mean_seq_len": round(float(lens1.mean()), 1),
             "max_seq_len": int(lens1.max()), "num_blocks": w.num_blocks,
             "partition_tokens": ptok, "max_partitions": nparts, "pool_replicas": R,
-            "step": (f"paged_attn_decode_append{'_planned' if planned else ''}{'_fp8' if fp8 else ''}: one call "
+            "step": (f"paged_attn_decode_append{'_fp8' if fp8 else ''}{'_planned' if planned else ''}: one call "
                      f"writes the new token (1 per seq) and decodes seq_len+1"
                      + (" (work order built on the host from the host copy of the lengths, every call)"
                         if planned else "") if fused else
@@ -588,7 +589,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "traffic_source": traffic_source,
                      "kernel": ("paged_attn_decode_append" if fused else "paged_attn_decode")
-                               + ("_planned" if planned else "") + ("_fp8" if fp8 else "")
+                               + ("_fp8" if fp8 else "") + ("_planned" if planned else "")
                                + " call (decode kernel"
                                + (")" if nparts == 1 else
                                   ", partitions merged in-kernel)" if nparts <= FUSED_MERGE_PARTS else

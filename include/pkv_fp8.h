@@ -94,6 +94,28 @@ PKV_API int pkv_paged_attn_decode_append_fp8(void *out, const void *q, void *k_p
                                              int32_t num_seqs, int32_t max_blocks_per_seq, int64_t num_blocks,
                                              int32_t dtype, void *stream);
 
+/*
+ * pkv_paged_attn_decode_append_fp8 with the lengths also in host memory, as
+ * pkv_paged_attn_decode_append_planned (pkv.h) is to the 16-bit step: the
+ * library builds the longest-first work order on the host from
+ * seq_lens_host (host memory, [num_seqs] int32, the values seq_lens holds on
+ * the device; read during the call only, owned by the caller;
+ * PKV_ERR_INVALID if null while num_seqs > 0) and the kernel skips its own.
+ * Used for batches of at most 256 sequences and at most 1024 work items per
+ * KV head, where a workgroup may take more than one item. Results are those
+ * of pkv_paged_attn_decode_append_fp8 bit for bit; a sequence whose device
+ * length splits into a different number of partitions than its host length
+ * gets NaN rows and no write, other sequences are unaffected.
+ */
+PKV_API int pkv_paged_attn_decode_append_fp8_planned(void *out, const void *q, void *k_pool, void *v_pool,
+                                                     const void *k_new, const void *v_new, const float *k_scale,
+                                                     const float *v_scale, const int32_t *block_tables,
+                                                     const int32_t *seq_lens, const int32_t *seq_lens_host,
+                                                     float scale, int32_t n_heads, int32_t n_kv_heads,
+                                                     int32_t head_dim, int32_t block_size, int32_t num_seqs,
+                                                     int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
+                                                     void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -80,6 +80,9 @@ _SIGNATURES = {
                                               _i64, _i32, _vp]),
     "pkv_paged_attn_decode_append_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32,
                                                         _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
+    "pkv_paged_attn_decode_append_fp8_planned": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                                _vp, _f32, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
+                                                                _i32, _vp]),
 }
 
 
@@ -599,11 +602,15 @@ def paged_attn_decode_append(out, q, k_pool, v_pool, k_new, v_new, block_tables,
 
 def paged_attn_decode_append_fp8(out, q, k_pool, v_pool, k_new, v_new, k_scale, v_scale, block_tables, seq_lens,
                                  scale: float, n_heads: int, n_kv_heads: int, head_dim: int, block_size: int,
-                                 stream=None):
+                                 stream=None, seq_lens_host=None):
     """One decode step over FP8 pools (uint8 e4m3 codes ``[NB, Hkv, BS, D]``,
     float32 scales ``[Hkv]``): encode and store each sequence's newest token
     (``k_new``/``v_new`` ``[B, Hkv, D]`` in the query dtype) at position
-    ``seq_lens - 1`` of its table, then decode over ``seq_lens`` tokens."""
+    ``seq_lens - 1`` of its table, then decode over ``seq_lens`` tokens.
+
+    ``seq_lens_host`` (optional): the same lengths as a C-contiguous int32
+    numpy array in host memory; the call is then
+    ``pkv_paged_attn_decode_append_fp8_planned``."""
     dt = q.dtype
     _need(dt in (torch.float16, torch.bfloat16), f"FP8 pools need an fp16/bf16 query, got {dt}")
     for name, t in (("out", out), ("q", q), ("k_new", k_new), ("v_new", v_new)):
@@ -625,12 +632,24 @@ def paged_attn_decode_append_fp8(out, q, k_pool, v_pool, k_new, v_new, k_scale, 
     _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B, MB]")
     devs = {t.device for t in (out, q, k_pool, v_pool, k_new, v_new, k_scale, v_scale, block_tables, seq_lens)}
     _need(len(devs) == 1, "all tensors must be on one device")
+    if seq_lens_host is not None:
+        _need(isinstance(seq_lens_host, np.ndarray) and seq_lens_host.dtype == np.int32
+              and seq_lens_host.shape == (B,) and seq_lens_host.flags["C_CONTIGUOUS"],
+              "seq_lens_host must be a C-contiguous int32 numpy array of shape [B]")
     with torch.cuda.device(q.device):
-        _check(lib().pkv_paged_attn_decode_append_fp8(
-            out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
-            k_scale.data_ptr(), v_scale.data_ptr(), block_tables.data_ptr(), seq_lens.data_ptr(), float(scale),
-            n_heads, n_kv_heads, head_dim, block_size, B, block_tables.shape[1], k_pool.shape[0], DTYPE_CODES[dt],
-            _stream_handle(q, stream)))
+        if seq_lens_host is None:
+            _check(lib().pkv_paged_attn_decode_append_fp8(
+                out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_new.data_ptr(),
+                v_new.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(), block_tables.data_ptr(),
+                seq_lens.data_ptr(), float(scale), n_heads, n_kv_heads, head_dim, block_size, B,
+                block_tables.shape[1], k_pool.shape[0], DTYPE_CODES[dt], _stream_handle(q, stream)))
+        else:
+            _check(lib().pkv_paged_attn_decode_append_fp8_planned(
+                out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_new.data_ptr(),
+                v_new.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(), block_tables.data_ptr(),
+                seq_lens.data_ptr(), seq_lens_host.ctypes.data, float(scale), n_heads, n_kv_heads, head_dim,
+                block_size, B, block_tables.shape[1], k_pool.shape[0], DTYPE_CODES[dt],
+                _stream_handle(q, stream)))
     return out
 
 

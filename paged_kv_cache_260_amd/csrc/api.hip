@@ -416,6 +416,19 @@ int pkv_paged_attn_decode_append_fp8(void *out, const void *q, void *k_pool, voi
                      k_new, v_new);
 }
 
+int pkv_paged_attn_decode_append_fp8_planned(void *out, const void *q, void *k_pool, void *v_pool,
+                                             const void *k_new, const void *v_new, const float *k_scale,
+                                             const float *v_scale, const int32_t *block_tables,
+                                             const int32_t *seq_lens, const int32_t *seq_lens_host, float scale,
+                                             int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                                             int32_t block_size, int32_t num_seqs, int32_t max_blocks_per_seq,
+                                             int64_t num_blocks, int32_t dtype, void *stream) {
+  if (num_seqs > 0 && !seq_lens_host) return fail(PKV_ERR_INVALID, "null seq_lens_host");
+  return decode_impl(out, q, k_pool, v_pool, block_tables, seq_lens, scale, n_heads, n_kv_heads, head_dim,
+                     block_size, num_seqs, max_blocks_per_seq, num_blocks, dtype, stream, true, k_scale, v_scale,
+                     k_new, v_new, false, seq_lens_host);
+}
+
 int pkv_paged_attn_decode_fp8(void *out, const void *q, const void *k_pool, const void *v_pool,
                               const float *k_scale, const float *v_scale, const int32_t *block_tables,
                               const int32_t *seq_lens, float scale, int32_t n_heads, int32_t n_kv_heads,

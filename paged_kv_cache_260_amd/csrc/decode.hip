@@ -1676,9 +1676,9 @@ namespace {
 constexpr int kWgsPerSlot = 2;
 
 // The longest-first order of make_plan, built on the host from the host
-// copy of the lengths, for launches whose workgroups take one item each
-// (tickets on, no more items per unit than workgroups). Leaves hp_items at
-// zero, and the kernel on its own plan, when the order does not fit the
+// copy of the lengths. With ticket claimers every workgroup must take one
+// item (no more items per unit than workgroups). Leaves hp_items at zero,
+// and the kernel on its own plan, when the order does not fit the
 // arguments.
 void host_plan(DecodeArgs &a) {
   const int B = a.num_seqs;
@@ -1695,7 +1695,7 @@ void host_plan(DecodeArgs &a) {
     bucket[s] = ok ? (int)((int64_t)(P - (L - full[s] * P)) * kRemBuckets / P) : kRemBuckets;
     items += full[s];
   }
-  if (items > kHostPlanItems || items > a.wgs_per_unit) return;
+  if (items > kHostPlanItems || (a.tickets && items > a.wgs_per_unit)) return;
   int n = 0;
   for (int s = 0; s < B; ++s) {
     for (int p = 0; p < full[s]; ++p) a.hp[n++] = (uint16_t)(s | (p << 8));
@@ -1743,11 +1743,13 @@ hipError_t launch_t(const DecodeArgs &args, hipStream_t stream) {
     a.tickets = nullptr;
   }
   a.hp_items = 0;
-  if constexpr (MODE == kModeAppend && !F8) {
-    if (a.host_seq_lens && a.tickets) host_plan(a);
+  // 16-bit pools: only where ticket claimers place every item (one item per
+  // workgroup); FP8 pools (no tickets, a workgroup may take two items): always
+  if constexpr (MODE == kModeAppend) {
+    if (a.host_seq_lens && (a.tickets || F8)) host_plan(a);
   }
   dim3 grid((unsigned)(units * a.wgs_per_unit), 1, 1);
-  if constexpr (MODE == kModeAppend && !F8) {
+  if constexpr (MODE == kModeAppend) {
     if (a.hp_items > 0)
       hipLaunchKernelGGL((paged_decode_kernel<T, D, GT, F8, MODE, true>), grid, dim3(kDecodeWaves * 64), 0, stream,
                          a);

@@ -96,6 +96,12 @@ def test_planned_append_rejects_bad_arguments(over, status):
     assert _lib.last_error() != ""
 
 
+def test_fp8_planned_append_rejects_null_host_lengths():
+    args = [16, 16, 16, 16, 16, 16, 16, 16, 16, 16, None, 0.125, 32, 8, 128, 16, 4, 8, 64, 2, None]
+    assert _lib.lib().pkv_paged_attn_decode_append_fp8_planned(*args) == _lib.PKV_ERR_INVALID
+    assert "seq_lens_host" in _lib.last_error()
+
+
 def test_planned_append_empty_batch_is_noop():
     assert _planned(num_seqs=0, seq_lens_host=None, q=None, out=None) == _lib.PKV_OK
 

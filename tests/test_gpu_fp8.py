@@ -337,3 +337,59 @@ def test_fp8_decode_every_code_exact(dtype, append):
     assert np.array_equal(np.isnan(got), np.isnan(want))
     ok = ~np.isnan(want)
     assert np.array_equal(got[ok], want[ok])   # -0.0 == 0.0 here: the sum's sign of zero is not a code value
+
+
+def _append_fp8(w, kc, vc, ks, vs, lens, host_lens=None):
+    dev = "cuda"
+    q = w.q.to(dev)
+    kp, vp = torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev)
+    out = torch.full_like(q, float("nan"))
+    _lib.paged_attn_decode_append_fp8(out, q, kp, vp, w.k_new.to(dev), w.v_new.to(dev), torch.from_numpy(ks).to(dev),
+                                      torch.from_numpy(vs).to(dev), torch.from_numpy(w.block_tables).to(dev),
+                                      torch.from_numpy(np.asarray(lens, np.int32)).to(dev), w.scale, w.n_heads,
+                                      w.n_kv_heads, w.head_dim, w.block_size,
+                                      seq_lens_host=None if host_lens is None else np.asarray(host_lens, np.int32))
+    torch.cuda.synchronize()
+    return out, kp, vp
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 5])
+def test_fp8_planned_append_equals_append(cfg):
+    """The planned FP8 step (work order built on the host; workgroups may take
+    two items) gives the one-call FP8 step's bits, output and pools, on the
+    MHA, GQA and shared-prompt workloads."""
+    say(f"fp8 planned append cfg{cfg}")
+    w = workloads.make(cfg, poison=True)
+    kc, vc, ks, vs = fp8_case(w, cfg)
+    lens = w.seq_lens_after_write()
+    out, kp, vp = _append_fp8(w, kc, vc, ks, vs, lens)
+    out2, kp2, vp2 = _append_fp8(w, kc, vc, ks, vs, lens, host_lens=lens)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(kp, kp2) and torch.equal(vp, vp2)
+
+
+def test_fp8_planned_append_host_length_mismatch():
+    """A host length that adds a partition gives NaN rows and no write for
+    that sequence; the other rows keep their bits, and the next planned call
+    with the right lengths gives the one-call step's bits again."""
+    w = workloads.random_case(7200, num_seqs=64, n_heads=32, n_kv_heads=8, head_dim=128, block_size=16,
+                              dtype=torch.bfloat16, max_len=1500, min_len=16, poison=True)
+    kc, vc, ks, vs = fp8_case(w, 7200)
+    lens = w.seq_lens_after_write()
+    cap = w.block_tables.shape[1] * w.block_size
+    P, _ = _lib.decode_plan(w.n_heads, w.n_kv_heads, w.block_size, w.num_seqs, w.block_tables.shape[1])
+    cand = [int(s) for s in np.flatnonzero((lens > 64) & (lens <= P) & (lens + P <= cap))]
+    assert cand
+    bad = cand[0]
+    host = lens.copy()
+    host[bad] = lens[bad] + P
+    say(f"fp8 mismatch: NaN rows for {bad}")
+    ref, kref, _ = _append_fp8(w, kc, vc, ks, vs, lens)
+    out, kp, _ = _append_fp8(w, kc, vc, ks, vs, lens, host_lens=host)
+    good = [s for s in range(w.num_seqs) if s != bad]
+    assert torch.isnan(out[bad].float()).all()
+    assert torch.equal(out[good].view(torch.int16), ref[good].view(torch.int16))
+    blk, off = divmod(int(w.slot_mapping[bad]), w.block_size)
+    assert np.array_equal(kp[blk, :, off].cpu().numpy(), kc[blk, :, off])
+    out3, _, _ = _append_fp8(w, kc, vc, ks, vs, lens, host_lens=lens)
+    assert torch.equal(out3.view(torch.int16), ref.view(torch.int16))
