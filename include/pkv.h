@@ -189,11 +189,14 @@ PKV_API int pkv_paged_attn_decode_append(void *out, const void *q, void *k_pool,
  *                   on the device; read during the call only, owned by the
  *                   caller (PKV_ERR_INVALID if null while num_seqs > 0)
  * Results are those of pkv_paged_attn_decode_append, bit for bit. The order
- * is used when the batch has at most 256 sequences and every workgroup takes
- * one item; other batches take the kernel's own order. A sequence whose
- * device length splits into a different number of partitions than its host
- * length gets NaN rows and its new token is not stored (one with the same
- * count is attended over its device length); other sequences are unaffected.
+ * is used when the batch has at most 256 sequences, every workgroup takes
+ * one item and a sequence has at most 8 partitions (pkv_decode_plan; they
+ * are then merged inside the kernel); other batches take the kernel's own
+ * order and read seq_lens_host no further. Where the order is used, a
+ * sequence whose device length splits into a different number of
+ * partitions than its host length gets NaN rows and its new token is not
+ * stored (one with the same count is attended over its device length);
+ * other sequences are unaffected.
  */
 PKV_API int pkv_paged_attn_decode_append_planned(void *out, const void *q, void *k_pool, void *v_pool,
                                                  const void *k_new, const void *v_new, const int32_t *block_tables,

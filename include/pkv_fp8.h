@@ -101,11 +101,13 @@ PKV_API int pkv_paged_attn_decode_append_fp8(void *out, const void *q, void *k_p
  * seq_lens_host (host memory, [num_seqs] int32, the values seq_lens holds on
  * the device; read during the call only, owned by the caller;
  * PKV_ERR_INVALID if null while num_seqs > 0) and the kernel skips its own.
- * Used for batches of at most 256 sequences and at most 1024 work items per
- * KV head, where a workgroup may take more than one item. Results are those
- * of pkv_paged_attn_decode_append_fp8 bit for bit; a sequence whose device
- * length splits into a different number of partitions than its host length
- * gets NaN rows and no write, other sequences are unaffected.
+ * Used for batches of at most 256 sequences, at most 1024 work items per KV
+ * head and at most 8 partitions per sequence (merged inside the kernel),
+ * where a workgroup may take more than one item; other batches take the
+ * kernel's own order. Results are those of pkv_paged_attn_decode_append_fp8
+ * bit for bit; where the order is used, a sequence whose device length
+ * splits into a different number of partitions than its host length gets
+ * NaN rows and no write, other sequences are unaffected.
  */
 PKV_API int pkv_paged_attn_decode_append_fp8_planned(void *out, const void *q, void *k_pool, void *v_pool,
                                                      const void *k_new, const void *v_new, const float *k_scale,

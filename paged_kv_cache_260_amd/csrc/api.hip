@@ -307,7 +307,6 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
   a.v_scale = v_scale;
   a.k_new = k_new;
   a.v_new = v_new;
-  a.host_seq_lens = host_seq_lens;
   plan(block_size, max_blocks_per_seq, &a.partition_tokens, &a.max_parts);
   if ((int64_t)num_seqs * a.max_parts * n_kv_heads * a.head_chunks > (int64_t)INT32_MAX)
     return fail(PKV_ERR_INVALID, "%d sequences x %d partitions x %d heads: too many workgroups",
@@ -316,6 +315,11 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
   // counters: the ticket counter of the late workgroups first, then (in-kernel
   // merge) the arrival counters; split partials: [acc rows x D | (m, l) rows]
   const bool fused_merge = a.max_parts > 1 && a.max_parts <= pkv::kFusedMergeParts;
+  // A host-built order only where partitions are merged inside the kernel (or
+  // there is one per sequence): a sequence whose host and device lengths
+  // disagree then writes its NaN rows and no partials, and no merge kernel can
+  // later combine stale partials of it into those rows.
+  a.host_seq_lens = a.max_parts == 1 || fused_merge ? host_seq_lens : nullptr;
   const int64_t counter_ints = kTicketInts + (fused_merge ? (int64_t)num_seqs * n_kv_heads * a.head_chunks : 0);
   const size_t rows = a.max_parts > 1 ? (size_t)num_seqs * n_heads * a.max_parts : 0;
   const size_t acc_bytes = rows * head_dim * sizeof(float);

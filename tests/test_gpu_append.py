@@ -243,3 +243,20 @@ def test_planned_append_host_length_mismatch():
     out3, _, _ = run_append(w, lens, host_lens=lens)
     out4, _, _ = run_append(w, lens)
     assert same_bits(out3, ref) and same_bits(out4, ref)
+
+
+def test_planned_append_long_tables_keep_the_kernel_order():
+    """Tables with more than 8 partitions per sequence merge in a separate
+    kernel, so the planned call does not use the host order there: host
+    lengths that disagree with the device's are not read, and the output and
+    pools are the one-call step's bits."""
+    w = workloads.random_case(7300, num_seqs=32, n_heads=32, n_kv_heads=8, head_dim=128, block_size=16,
+                              dtype=torch.bfloat16, max_len=9000, min_len=16, poison=True)
+    _, nparts = _lib.decode_plan(w.n_heads, w.n_kv_heads, w.block_size, w.num_seqs, w.block_tables.shape[1])
+    assert nparts > 8
+    lens = w.seq_lens_after_write()
+    host = lens.copy()
+    host[0] = lens[0] + 2048 if lens[0] + 2048 <= w.block_tables.shape[1] * w.block_size else 1
+    out, kp, vp = run_append(w, lens)
+    out2, kp2, vp2 = run_append(w, lens, host_lens=host)
+    assert same_bits(out, out2) and same_bits(kp, kp2) and same_bits(vp, vp2)

@@ -393,3 +393,21 @@ def test_fp8_planned_append_host_length_mismatch():
     assert np.array_equal(kp[blk, :, off].cpu().numpy(), kc[blk, :, off])
     out3, _, _ = _append_fp8(w, kc, vc, ks, vs, lens, host_lens=lens)
     assert torch.equal(out3.view(torch.int16), ref.view(torch.int16))
+
+
+def test_fp8_planned_append_long_tables_keep_the_kernel_order():
+    """More than 8 partitions per sequence (a separate merge kernel): the
+    planned FP8 call keeps the kernel's own order and ignores host lengths
+    that disagree; the bits are the one-call FP8 step's."""
+    w = workloads.random_case(7400, num_seqs=8, n_heads=32, n_kv_heads=8, head_dim=128, block_size=16,
+                              dtype=torch.bfloat16, max_len=12000, min_len=2000, poison=True)
+    _, nparts = _lib.decode_plan(w.n_heads, w.n_kv_heads, w.block_size, w.num_seqs, w.block_tables.shape[1])
+    assert nparts > 8
+    kc, vc, ks, vs = fp8_case(w, 7400)
+    lens = w.seq_lens_after_write()
+    host = lens.copy()
+    host[0] = 1
+    out, kp, vp = _append_fp8(w, kc, vc, ks, vs, lens)
+    out2, kp2, vp2 = _append_fp8(w, kc, vc, ks, vs, lens, host_lens=host)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(kp, kp2) and torch.equal(vp, vp2)
