@@ -45,6 +45,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <climits>
 #include <atomic>
 
 namespace pkv {
@@ -1676,23 +1677,29 @@ namespace {
 constexpr int kWgsPerSlot = 2;
 
 // The longest-first order of make_plan, built on the host from the host
-// copy of the lengths. With ticket claimers every workgroup must take one
-// item (no more items per unit than workgroups). Leaves hp_items at zero,
-// and the kernel on its own plan, when the order does not fit the
-// arguments.
-void host_plan(DecodeArgs &a) {
+// copy of the lengths: the full partitions (sequence-major), then the last
+// partitions by decreasing length, in sequence order among equals. exact:
+// by their exact length, where make_plan takes kRemBuckets buckets (with
+// one item per workgroup the exact order measured faster; FP8 pools, whose
+// workgroups walk two items, keep the buckets). With ticket claimers every
+// workgroup must take one item (no more items per unit than workgroups).
+// Leaves hp_items at zero, and the kernel on its own plan, when the order
+// does not fit the arguments.
+void host_plan(DecodeArgs &a, bool exact) {
   const int B = a.num_seqs;
   const int P = a.partition_tokens;
   const int64_t max_tok = (int64_t)a.max_blocks * a.block_size;
   if (B > kHostPlanSeqs || P < 1) return;
-  int full[kHostPlanSeqs], bucket[kHostPlanSeqs];
+  int full[kHostPlanSeqs], key[kHostPlanSeqs], order[kHostPlanSeqs];
   int64_t items = B;
   for (int s = 0; s < B; ++s) {
     const int L = a.host_seq_lens[s];
     const bool ok = L > 0 && (int64_t)L <= max_tok;
     full[s] = ok ? (L - 1) / P : 0;
     if (full[s] + 1 > 255) return;  // partition ids take 8 bits
-    bucket[s] = ok ? (int)((int64_t)(P - (L - full[s] * P)) * kRemBuckets / P) : kRemBuckets;
+    const int shortfall = P - (L - full[s] * P);  // 0 .. P - 1 when ok
+    key[s] = !ok ? INT_MAX : exact ? shortfall : (int)((int64_t)shortfall * kRemBuckets / P);
+    order[s] = s;
     items += full[s];
   }
   if (items > kHostPlanItems || (a.tickets && items > a.wgs_per_unit)) return;
@@ -1701,9 +1708,8 @@ void host_plan(DecodeArgs &a) {
     for (int p = 0; p < full[s]; ++p) a.hp[n++] = (uint16_t)(s | (p << 8));
     a.hp_np[s] = (uint8_t)(full[s] + 1);
   }
-  for (int b = 0; b <= kRemBuckets; ++b)
-    for (int s = 0; s < B; ++s)
-      if (bucket[s] == b) a.hp[n++] = (uint16_t)(s | (full[s] << 8));
+  std::stable_sort(order, order + B, [&](int x, int y) { return key[x] < key[y]; });
+  for (int i = 0; i < B; ++i) a.hp[n++] = (uint16_t)(order[i] | (full[order[i]] << 8));
   a.hp_items = n;
 }
 
@@ -1746,7 +1752,7 @@ hipError_t launch_t(const DecodeArgs &args, hipStream_t stream) {
   // 16-bit pools: only where ticket claimers place every item (one item per
   // workgroup); FP8 pools (no tickets, a workgroup may take two items): always
   if constexpr (MODE == kModeAppend) {
-    if (a.host_seq_lens && (a.tickets || F8)) host_plan(a);
+    if (a.host_seq_lens && (a.tickets || F8)) host_plan(a, !F8);
   }
   dim3 grid((unsigned)(units * a.wgs_per_unit), 1, 1);
   if constexpr (MODE == kModeAppend) {
